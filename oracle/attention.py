@@ -1,0 +1,104 @@
+"""Plain fp64 CPU attention forward: the oracle that parity tests trust.
+
+TEST INFRASTRUCTURE ONLY. Only the test suite, the smoke check and the
+benchmark's CPU-baseline leg may import this module. The product path never
+calls it, and it imports nothing from the HIP package.
+
+What it computes, per batch b, head h and query row i (sources are the pages
+this project is built from):
+
+* "[GPU] Deep Learning for HPC", section "Flash Attention": attention multiplies
+  Q by K transposed to form the score matrix, applies softmax to it, then
+  multiplies the result by V.
+* null-ptr.tistory.com, category "development", teaser of the softmax post:
+  softmax_i(z) = e^{z_i} / sum_j e^{z_j}; the exponential overflows for large
+  inputs, so the maximum is subtracted first (the text is cut off; this is the
+  standard reading and it leaves the value unchanged).
+* Same page, teaser of the Triton FlashAttention post: the forward kernel takes
+  a ``softmax_scale``, an ``IS_CAUSAL`` flag and writes ``Out`` and ``Lse``.
+
+Readings taken where the pages are silent (each is listed in the design notes):
+
+* ``scale`` multiplies Q K^T before masking and softmax.
+* causal: key j is visible to query i iff j <= i (queries and keys share one
+  position axis); masked keys get weight exactly 0.
+* lse is the natural log of sum_j exp(s_ij) over the visible keys, using the
+  scaled scores.
+
+The score row is materialised in full (no online recurrence, no tiling), rows
+are processed in chunks only to bound memory.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = ["attend_head", "attention_ref"]
+
+
+def attend_head(q, k, v, scale, causal, q_pos=None, return_weights=False,
+                chunk=1024):
+    """Attention of one head: returns (o [M,d], lse [M]) in float64.
+
+    q: [M, d] query rows; k, v: [N, d] keys and values of the head.
+    scale: the softmax scale (used as given, widened to float64).
+    causal: if true, query row r sees keys 0..q_pos[r] only.
+    q_pos: position of each query row on the key axis (default 0..M-1, i.e. the
+      rows are the head's first M queries). Lets a test check a sample of rows.
+    return_weights: also return the normalised weights [M, N] (debug aid).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    scale = float(scale)
+    m_rows, d = q.shape
+    n_keys = k.shape[0]
+    if k.shape != (n_keys, d) or v.shape[0] != n_keys:
+        raise ValueError("q, k, v shapes do not agree")
+    if q_pos is None:
+        q_pos = np.arange(m_rows)
+    q_pos = np.asarray(q_pos, dtype=np.int64)
+    if causal and m_rows and (q_pos.min() < 0 or q_pos.max() >= n_keys):
+        raise ValueError("causal query positions must lie on the key axis")
+
+    o = np.empty((m_rows, v.shape[1]), dtype=np.float64)
+    lse = np.empty(m_rows, dtype=np.float64)
+    weights = np.empty((m_rows, n_keys), dtype=np.float64) if return_weights else None
+    key_idx = np.arange(n_keys)
+    for r0 in range(0, m_rows, chunk):
+        r1 = min(r0 + chunk, m_rows)
+        # scores s_ij = scale * <q_i, k_j> over the full key axis
+        s = scale * (q[r0:r1] @ k.T)
+        if causal:
+            hidden = key_idx[None, :] > q_pos[r0:r1, None]
+            s[hidden] = -np.inf
+        # safe softmax: subtract the row maximum, exponentiate, normalise
+        m = s.max(axis=1, keepdims=True)
+        w = np.exp(s - m)  # masked entries: exp(-inf) == 0 exactly
+        l = w.sum(axis=1, keepdims=True)
+        o[r0:r1] = (w @ v) / l
+        lse[r0:r1] = m[:, 0] + np.log(l[:, 0])
+        if return_weights:
+            weights[r0:r1] = w / l
+    if return_weights:
+        return o, lse, weights
+    return o, lse
+
+
+def attention_ref(q, k, v, scale, causal):
+    """Attention over a [B, H, N, d] batch: returns (o [B,H,N,d], lse [B,H,N]).
+
+    Every (b, h) pair is an independent head; each is handed to attend_head.
+    """
+    q = np.asarray(q)
+    k = np.asarray(k)
+    v = np.asarray(v)
+    if q.ndim != 4 or k.shape != q.shape or v.shape[:3] != q.shape[:3]:
+        raise ValueError("expected q, k, v of shape [B, H, N, d]")
+    b_n, h_n, n, _ = q.shape
+    o = np.empty(v.shape, dtype=np.float64)
+    lse = np.empty((b_n, h_n, n), dtype=np.float64)
+    for b in range(b_n):
+        for h in range(h_n):
+            o[b, h], lse[b, h] = attend_head(q[b, h], k[b, h], v[b, h], scale, causal)
+    return o, lse
