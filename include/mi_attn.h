@@ -1,0 +1,91 @@
+/*
+ * mi_attn.h - C ABI of libmi_attn, a fused attention forward for MI355X (gfx950).
+ *
+ * The operation (sources: "[GPU] Deep Learning for HPC", section "Flash
+ * Attention" - scores Q K^T, softmax, times V, computed tile by tile without
+ * writing the score matrix out; null-ptr.tistory.com, category "development",
+ * the Triton FlashAttention post - a forward kernel taking Q, K, V, a softmax
+ * scale and a causal flag and writing Out and Lse), for every batch b, head h
+ * and query row i:
+ *
+ *     s_ij   = scale * sum_t q_it * k_jt          for visible keys j
+ *     o_i    = sum_j exp(s_ij) v_j / sum_j exp(s_ij)
+ *     lse_i  = ln sum_j exp(s_ij)                 (natural log, scaled scores)
+ *
+ * where every key is visible when causal == 0, and key j is visible to query i
+ * iff j <= i when causal != 0. Masked keys carry weight exactly zero.
+ *
+ * All calls are thread-safe, keep no state between calls, allocate nothing,
+ * never print and never abort.
+ */
+#ifndef MI_ATTN_H
+#define MI_ATTN_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. Every entry point returns one; 0 is success. */
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_NULL = -1,      /* a required pointer (q, k, v, o, lse, or an out-param) is NULL */
+  ATTN_ERR_SHAPE = -2,     /* B, H or N negative, or B*H*N*d overflows int64 / the grid */
+  ATTN_ERR_HEADDIM = -3,   /* d is neither 64 nor 128 */
+  ATTN_ERR_ALIGN = -5,     /* q, k, v or o not 16-byte aligned, or lse not 4-byte aligned */
+  ATTN_ERR_ALIAS = -6,     /* o or lse overlaps an input, or o overlaps lse */
+  ATTN_ERR_SCALE = -7,     /* scale is NaN or infinite */
+  ATTN_ERR_LAUNCH = -8     /* the HIP launch failed (no gfx950 device, bad stream, ...) */
+} attn_status;
+
+/*
+ * attn_fwd - attention forward with per-row log-sum-exp.
+ *
+ *   q, k, v  device pointers to bf16 tensors [B, H, N, d], contiguous row-major
+ *            (d fastest, then N, then H, then B). Read only.
+ *   o        device pointer to a bf16 tensor [B, H, N, d], same layout; written.
+ *   lse      device pointer to a float32 tensor [B, H, N]; written.
+ *   B, H, N  batch size, heads, sequence length (queries and keys share N).
+ *            Any N >= 1 is accepted (no multiple-of-tile restriction). If
+ *            B*H*N == 0 the call does nothing and returns ATTN_OK.
+ *   d        head dimension: 64 or 128.
+ *   scale    softmax scale, applied to Q K^T before masking; used exactly as
+ *            the given float32 value. Any finite value (0 and negative
+ *            included) is accepted.
+ *   causal   0: every key visible. Non-zero: key j visible to query i iff j <= i.
+ *   stream   hipStream_t to launch on; NULL means the null stream.
+ *
+ * Ownership: the caller allocates and frees every buffer; all device pointers
+ * must belong to the current device. The call is asynchronous: it only queues
+ * one kernel on `stream` and returns; the caller synchronises before reading
+ * o and lse. Arithmetic: bf16 products accumulated in fp32, the softmax
+ * weights rounded to bf16 before the P*V product, o rounded to bf16 (nearest
+ * even), lse in fp32. Results are deterministic (no atomics).
+ *
+ * Errors: arguments are validated before any HIP call. On a validation error
+ * nothing is launched and o, lse are untouched. ATTN_ERR_LAUNCH reports the
+ * status of the launch itself. NaN or Inf inside q, k, v propagate.
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int B, int H, int N, int d, float scale, int causal, void* stream);
+
+/* attn_strerror - static, NUL-terminated description of a status code
+ * (an unknown code yields "unknown status"). Never NULL. */
+const char* attn_strerror(int status);
+
+/*
+ * attn_fwd_launch_shape - the launch attn_fwd would make for these sizes,
+ * without launching: workgroups in the 1-D grid, threads per workgroup, LDS
+ * bytes per workgroup, query rows per workgroup (block_m) and keys per inner
+ * step (block_n). Out-params may not be NULL. Returns the same validation
+ * status attn_fwd would for the sizes (pointers are not examined); on error
+ * the out-params are untouched. For B*H*N == 0 it returns ATTN_OK with
+ * *grid == 0.
+ */
+int attn_fwd_launch_shape(int B, int H, int N, int d, int causal, int* grid,
+                          int* block, int* lds_bytes, int* block_m, int* block_n);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MI_ATTN_H */

@@ -1,0 +1,171 @@
+"""The C ABI of libmi_attn, checked without a GPU.
+
+Every call here fails validation (or is the empty no-op), which the library
+does before any HIP call, so nothing is launched. The pointers are stand-in
+integers that are never dereferenced.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import tiled_attention_forward_02_amd as mi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mi_attn.h")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_HEADDIM, ERR_ALIGN, ERR_ALIAS, ERR_SCALE, ERR_LAUNCH = (
+    0, -1, -2, -3, -5, -6, -7, -8)
+
+MIB = 1 << 20
+# Stand-in device addresses, 1 MiB apart and 256-byte aligned.
+Q, K, V, O, L = (0x7f0000000000 + i * 64 * MIB for i in range(5))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    try:
+        return mi.load_library()
+    except ImportError as e:  # the build step did not run
+        pytest.fail(str(e))
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\([^;{]*\)\s*;", text)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == ["attn_fwd", "attn_fwd_launch_shape", "attn_strerror"]
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_no_extra_exported_c_symbols():
+    """Only the header's functions carry C linkage (nm -D of the library)."""
+    import shutil
+    import subprocess
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm not available")
+    out = subprocess.run([nm, "-D", "--defined-only", mi.lib_path()],
+                         capture_output=True, text=True, check=True).stdout
+    syms = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    c_syms = {s for s in syms if s.startswith("attn_")}
+    assert c_syms == set(declared_functions())
+
+
+def test_strerror_covers_every_status(lib):
+    seen = set()
+    for code in (OK, ERR_NULL, ERR_SHAPE, ERR_HEADDIM, ERR_ALIGN, ERR_ALIAS,
+                 ERR_SCALE, ERR_LAUNCH):
+        msg = mi.attn_strerror(code)
+        assert msg and msg != "unknown status"
+        seen.add(msg)
+    assert len(seen) == 8
+    assert mi.attn_strerror(12345) == "unknown status"
+
+
+def call(lib, q=Q, k=K, v=V, o=O, lse=L, B=2, H=3, N=100, d=64, scale=0.125,
+         causal=0):
+    return lib.attn_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, None)
+
+
+@pytest.mark.parametrize("which", ["q", "k", "v", "o", "lse"])
+def test_null_pointer(lib, which):
+    assert call(lib, **{which: None}) == ERR_NULL
+
+
+@pytest.mark.parametrize("B,H,N", [(-1, 1, 1), (1, -2, 1), (1, 1, -5)])
+def test_negative_sizes(lib, B, H, N):
+    assert call(lib, B=B, H=H, N=N) == ERR_SHAPE
+
+
+def test_size_overflow(lib):
+    big = 2**31 - 1
+    assert call(lib, B=big, H=big, N=big, d=128) == ERR_SHAPE
+
+
+@pytest.mark.parametrize("d", [0, 1, 16, 32, 63, 65, 96, 127, 129, 256])
+def test_unsupported_head_dim(lib, d):
+    assert call(lib, d=d) == ERR_HEADDIM
+
+
+@pytest.mark.parametrize("which,offset", [("q", 8), ("k", 2), ("v", 4), ("o", 12),
+                                          ("lse", 2)])
+def test_misaligned(lib, which, offset):
+    base = {"q": Q, "k": K, "v": V, "o": O, "lse": L}[which]
+    assert call(lib, **{which: base + offset}) == ERR_ALIGN
+
+
+def test_lse_four_byte_alignment_is_enough(lib):
+    # lse at +4 passes alignment; o aliasing q then trips the next check,
+    # so nothing is launched.
+    assert call(lib, lse=L + 4, o=Q) == ERR_ALIAS
+
+
+@pytest.mark.parametrize("o,lse", [(Q, L), (K + 256, L), (V, L), (O, Q + 16),
+                                   (O, O + 64)])
+def test_aliasing(lib, o, lse):
+    assert call(lib, o=o, lse=lse) == ERR_ALIAS
+
+
+def test_inputs_may_alias_each_other_but_outputs_not(lib):
+    # q == k == v is legal; with o == q the call is rejected before launch.
+    assert call(lib, k=Q, v=Q, o=Q) == ERR_ALIAS
+
+
+@pytest.mark.parametrize("scale", [float("nan"), float("inf"), float("-inf")])
+def test_non_finite_scale(lib, scale):
+    assert call(lib, scale=scale) == ERR_SCALE
+
+
+@pytest.mark.parametrize("B,H,N", [(0, 4, 128), (2, 0, 128), (2, 4, 0)])
+def test_empty_is_a_no_op(lib, B, H, N):
+    # Nothing to compute: success without touching the (null) pointers.
+    assert call(lib, q=None, k=None, v=None, o=None, lse=None, B=B, H=H, N=N) == OK
+
+
+def test_validation_order(lib):
+    # size errors come before pointer errors
+    assert call(lib, q=None, d=96) == ERR_HEADDIM
+    assert call(lib, q=None, N=-1) == ERR_SHAPE
+
+
+@pytest.mark.parametrize("B,H,N,d,causal", [
+    (1, 1, 128, 64, 0), (4, 16, 1024, 64, 0), (8, 16, 2048, 64, 1),
+    (16, 16, 4096, 128, 0), (1, 32, 16384, 128, 1), (2, 3, 1, 64, 0),
+    (2, 3, 129, 128, 1)])
+def test_launch_shape(lib, B, H, N, d, causal):
+    s = mi.attn_fwd_launch_shape(B, H, N, d, causal)
+    bm = s["block_m"]
+    assert s["grid"] == B * H * ((N + bm - 1) // bm)
+    assert s["block"] % 64 == 0 and s["block"] <= 1024
+    assert s["block_n"] * d == 8192
+    assert 0 < s["lds_bytes"] <= 160 * 1024
+
+
+def test_launch_shape_errors(lib):
+    with pytest.raises(mi.AttnError):
+        mi.attn_fwd_launch_shape(1, 1, 128, 80)
+    out = [ctypes.c_int(0) for _ in range(4)]
+    assert lib.attn_fwd_launch_shape(1, 1, 128, 64, 0, None,
+                                     *[ctypes.byref(x) for x in out]) == ERR_NULL
+    assert mi.attn_fwd_launch_shape(0, 1, 128, 64)["grid"] == 0
+
+
+def test_binding_rejects_bad_tensors():
+    import torch
+    q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):  # CPU tensors never reach the library
+        mi.attn_fwd(q, q, q)
+    with pytest.raises(TypeError):
+        mi.attn_fwd(q.float(), q, q)
+    with pytest.raises(TypeError):
+        mi.attn_fwd([1], q, q)

@@ -1,0 +1,230 @@
+"""Parity of the HIP attention forward against the fp64 oracle (GPU only).
+
+The bar, for bf16 inputs with fp32 accumulation: max |O - O_ref| <= 2e-2 and
+max |lse - lse_ref| <= 1e-3, element by element, on the same seeded inputs.
+Every call goes through the C ABI (the ctypes binding). Each GPU step prints
+the case it runs first, so a failing run names it.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import tiled_attention_forward_02_amd as mi
+from oracle import attend_head, attention_ref
+from tiled_attention_forward_02_amd.workloads import WORKLOADS, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+O_TOL = 2e-2
+LSE_TOL = 1e-3
+
+
+def announce(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no HIP device")
+    mi.load_library()
+
+
+def run_gpu(inp, scale=None, causal=None, stream=None):
+    dev = torch.device("cuda:0")
+    q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+    o, lse = mi.attn_fwd(q, k, v, scale=inp["scale"] if scale is None else scale,
+                         causal=inp["causal"] if causal is None else causal,
+                         stream=stream)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy(), lse.cpu().numpy()
+
+
+def as64(t):
+    return t.to(torch.float64).numpy()
+
+
+def check(o, lse, o_ref, lse_ref, what):
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse)), f"{what}: non-finite output"
+    eo = float(np.abs(o - o_ref).max()) if o.size else 0.0
+    el = float(np.abs(lse - lse_ref).max()) if lse.size else 0.0
+    print(f"  {what}: max|dO|={eo:.3e} max|dlse|={el:.3e}", flush=True)
+    assert eo <= O_TOL, f"{what}: max |O - O_ref| = {eo}"
+    assert el <= LSE_TOL, f"{what}: max |lse - lse_ref| = {el}"
+
+
+# ---------------------------------------------- the five metric workloads --
+
+@pytest.mark.parametrize("idx", [1, 2, 3])
+def test_workload_full(idx):
+    """Small workloads: every output element against the oracle."""
+    w = WORKLOADS[idx - 1]
+    announce(f"workload {w.name} full compare")
+    inp = make_inputs(w)
+    o, lse = run_gpu(inp)
+    o_ref, lse_ref = attention_ref(as64(inp["q"]), as64(inp["k"]), as64(inp["v"]),
+                                   inp["scale"], w.causal)
+    check(o, lse, o_ref, lse_ref, w.name)
+
+
+@pytest.mark.parametrize("idx", [4, 5])
+def test_workload_sampled(idx):
+    """Full-size workloads in the benchmark's launch: whole heads for a few
+    (b, h) pairs plus sampled query rows from every head, each computed by
+    the oracle one row at a time against that head's full K and V."""
+    w = WORKLOADS[idx - 1]
+    announce(f"workload {w.name} sampled compare")
+    inp = make_inputs(w)
+    o, lse = run_gpu(inp)
+    q, k, v = inp["q"], inp["k"], inp["v"]
+    rng = np.random.default_rng(1234 + idx)
+    full_heads = [(0, 0), (w.B - 1, w.H - 1)]
+    for b, h in full_heads:
+        o_ref, lse_ref = attend_head(as64(q[b, h]), as64(k[b, h]), as64(v[b, h]),
+                                     inp["scale"], w.causal)
+        check(o[b, h], lse[b, h], o_ref, lse_ref, f"{w.name} head ({b},{h})")
+    rows_per_head = 8 if w.B * w.H > 64 else 24
+    for b in range(w.B):
+        for h in range(w.H):
+            rows = np.sort(rng.choice(w.N, rows_per_head, replace=False))
+            rows[0] = w.N - 1  # always include the last row (longest causal prefix)
+            o_ref, lse_ref = attend_head(as64(q[b, h][rows]), as64(k[b, h]),
+                                         as64(v[b, h]), inp["scale"], w.causal,
+                                         q_pos=rows)
+            check(o[b, h][rows], lse[b, h][rows], o_ref, lse_ref,
+                  f"{w.name} rows of ({b},{h})")
+
+
+# ------------------------------------------- ragged and small shapes --
+
+RAGGED = [(1, 1, 1), (1, 2, 17), (2, 3, 100), (1, 2, 127), (1, 1, 129), (2, 2, 300),
+          (1, 3, 513), (1, 1, 1000), (3, 5, 64), (1, 1, 256)]
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("B,H,N", RAGGED)
+def test_ragged(B, H, N, d, causal):
+    """Any N: partial query tiles, partial key tiles, N below one tile."""
+    announce(f"ragged B={B} H={H} N={N} d={d} causal={causal}")
+    w = WORKLOADS[1]
+    inp = make_inputs(w, B=B, H=H, N=N, d=d, seed=1000 + N + d)
+    o, lse = run_gpu(inp, causal=causal)
+    o_ref, lse_ref = attention_ref(as64(inp["q"]), as64(inp["k"]), as64(inp["v"]),
+                                   inp["scale"], causal)
+    check(o, lse, o_ref, lse_ref, f"N={N} d={d} causal={causal}")
+
+
+# ------------------------------------------------ closed forms on the GPU --
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_zero_query_gives_mean_of_visible_values(d, causal):
+    announce(f"Q=0 d={d} causal={causal}")
+    inp = make_inputs(WORKLOADS[1], B=1, H=2, N=333, d=d, seed=7)
+    inp["q"] = torch.zeros_like(inp["q"])
+    o, lse = run_gpu(inp, causal=causal)
+    v = as64(inp["v"])
+    n = np.arange(1, 334)
+    if causal:
+        o_ref = np.cumsum(v, axis=2) / n[None, None, :, None]
+        lse_ref = np.broadcast_to(np.log(n), lse.shape)
+    else:
+        o_ref = np.broadcast_to(v.mean(axis=2, keepdims=True), v.shape)
+        lse_ref = np.full(lse.shape, math.log(333))
+    check(o, lse, o_ref, lse_ref, "Q=0")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_zero_scale(causal):
+    announce(f"scale=0 causal={causal}")
+    inp = make_inputs(WORKLOADS[1], B=1, H=2, N=200, d=64, seed=8)
+    o, lse = run_gpu(inp, scale=0.0, causal=causal)
+    o_ref, lse_ref = attention_ref(as64(inp["q"]), as64(inp["k"]), as64(inp["v"]),
+                                   0.0, causal)
+    check(o, lse, o_ref, lse_ref, "scale=0")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_constant_values(causal):
+    announce(f"constant V causal={causal}")
+    inp = make_inputs(WORKLOADS[1], B=2, H=2, N=190, d=128, seed=9)
+    inp["v"] = torch.full_like(inp["v"], 0.375)
+    o, _ = run_gpu(inp, causal=causal)
+    assert np.abs(o - 0.375).max() <= O_TOL
+
+
+@pytest.mark.parametrize("scale", [-0.125, 0.9, -2.0, 5.0])
+@pytest.mark.parametrize("causal", [False, True])
+def test_other_scales(scale, causal):
+    """Negative scales and peaky softmax (large scale) follow the definition."""
+    announce(f"scale={scale} causal={causal}")
+    inp = make_inputs(WORKLOADS[1], B=1, H=2, N=257, d=64, seed=10)
+    o, lse = run_gpu(inp, scale=scale, causal=causal)
+    o_ref, lse_ref = attention_ref(as64(inp["q"]), as64(inp["k"]), as64(inp["v"]),
+                                   np.float32(scale), causal)
+    check(o, lse, o_ref, lse_ref, f"scale={scale}")
+
+
+def test_large_shift_of_keys():
+    """A big common shift of all keys leaves O unchanged (needs the running
+    maximum; scores reach about 2e2)."""
+    announce("key shift")
+    inp = make_inputs(WORKLOADS[3], B=1, H=1, N=300, d=128, seed=11)
+    inp["k"] = (inp["k"].float() + 16.0).to(torch.bfloat16)
+    inp["q"] = (inp["q"].float() + 1.0).to(torch.bfloat16)
+    o, lse = run_gpu(inp)
+    o_ref, lse_ref = attention_ref(as64(inp["q"]), as64(inp["k"]), as64(inp["v"]),
+                                   inp["scale"], False)
+    check(o, lse, o_ref, lse_ref, "key shift")
+
+
+# ------------------------------------------------------- runtime behaviour --
+
+def test_deterministic():
+    announce("determinism")
+    inp = make_inputs(WORKLOADS[2], B=2, H=4, N=700, d=64, seed=12)
+    o1, l1 = run_gpu(inp)
+    o2, l2 = run_gpu(inp)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_non_default_stream_and_preallocated_outputs():
+    announce("side stream")
+    inp = make_inputs(WORKLOADS[3], B=1, H=2, N=400, d=128, seed=13)
+    dev = torch.device("cuda:0")
+    q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+    out = torch.full_like(q, float("nan"))
+    lse = torch.full(q.shape[:3], float("nan"), device=dev)
+    s = torch.cuda.Stream(device=dev)
+    s.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(s):
+        mi.attn_fwd(q, k, v, scale=inp["scale"], causal=True, out=out, lse=lse)
+    s.synchronize()
+    o_ref, lse_ref = attention_ref(as64(inp["q"]), as64(inp["k"]), as64(inp["v"]),
+                                   inp["scale"], True)
+    check(out.float().cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref, "side stream")
+
+
+def test_empty_batch_is_a_no_op():
+    announce("empty")
+    dev = torch.device("cuda:0")
+    q = torch.zeros(0, 4, 128, 64, dtype=torch.bfloat16, device=dev)
+    o, lse = mi.attn_fwd(q, q, q)
+    torch.cuda.synchronize()
+    assert o.shape == q.shape and lse.shape == (0, 4, 128)
+
+
+def test_rejections_leave_outputs_untouched():
+    announce("rejection")
+    dev = torch.device("cuda:0")
+    q = torch.randn(1, 1, 64, 64, device=dev).to(torch.bfloat16)
+    out = torch.full_like(q, 7.0)
+    lse = torch.full((1, 1, 64), 7.0, device=dev)
+    with pytest.raises(mi.AttnError):
+        mi.attn_fwd(q, q, q, scale=float("nan"), out=out, lse=lse)
+    torch.cuda.synchronize()
+    assert bool((out == 7).all()) and bool((lse == 7).all())

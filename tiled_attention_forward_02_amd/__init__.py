@@ -1,0 +1,120 @@
+"""Python binding of libmi_attn: argument marshalling over the C ABI only.
+
+Every step of the attention forward runs in the HIP kernel behind
+``attn_fwd`` in libmi_attn.so; this module checks tensors, allocates the
+outputs with torch (device memory and streams are all torch provides here) and
+passes raw pointers. There is no fallback: if the shared library is missing
+the first call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+__all__ = ["attn_fwd", "attn_strerror", "attn_fwd_launch_shape", "lib_path",
+           "load_library", "AttnError"]
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmi_attn.so")
+_lib = None
+
+
+class AttnError(RuntimeError):
+    """A non-zero status returned by libmi_attn."""
+
+    def __init__(self, status, message):
+        super().__init__(f"attn_fwd failed ({status}): {message}")
+        self.status = status
+
+
+def lib_path():
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libmi_attn.so (once). Raises ImportError if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(
+            f"{_LIB_PATH} is missing: build it with "
+            "`python -m tiled_attention_forward_02_amd.build` (needs hipcc)")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i32, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, i32, vp]
+    lib.attn_fwd.restype = i32
+    lib.attn_strerror.argtypes = [i32]
+    lib.attn_strerror.restype = ctypes.c_char_p
+    ip = ctypes.POINTER(i32)
+    lib.attn_fwd_launch_shape.argtypes = [i32, i32, i32, i32, i32, ip, ip, ip, ip, ip]
+    lib.attn_fwd_launch_shape.restype = i32
+    _lib = lib
+    return lib
+
+
+def attn_strerror(status):
+    return load_library().attn_strerror(int(status)).decode()
+
+
+def attn_fwd_launch_shape(B, H, N, d, causal=False):
+    """The launch attn_fwd makes for these sizes, as a dict (no launch)."""
+    lib = load_library()
+    out = [ctypes.c_int(0) for _ in range(5)]
+    rc = lib.attn_fwd_launch_shape(B, H, N, d, int(bool(causal)),
+                                   *[ctypes.byref(x) for x in out])
+    if rc:
+        raise AttnError(rc, attn_strerror(rc))
+    return dict(zip(("grid", "block", "lds_bytes", "block_m", "block_n"),
+                    (x.value for x in out)))
+
+
+def attn_fwd(q, k, v, scale=None, causal=False, out=None, lse=None, stream=None):
+    """O, lse = attention forward of bf16 tensors q, k, v [B, H, N, d].
+
+    scale defaults to float32(1/sqrt(d)). ``out`` ([B,H,N,d] bf16) and ``lse``
+    ([B,H,N] float32) may be given to write into; otherwise they are allocated
+    on q's device. The kernel is queued on ``stream`` (default: torch's current
+    stream of q's device); nothing synchronises.
+    """
+    import torch
+
+    lib = load_library()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if t.dtype != torch.bfloat16:
+            raise TypeError(f"{name} must be bfloat16, got {t.dtype}")
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be on a HIP device, got {t.device}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous [B, H, N, d]")
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError(f"q, k, v must share one [B, H, N, d] shape, got "
+                         f"{tuple(q.shape)}, {tuple(k.shape)}, {tuple(v.shape)}")
+    if k.device != q.device or v.device != q.device:
+        raise ValueError("q, k, v must be on one device")
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32))
+    if out is None:
+        out = torch.empty_like(q)
+    elif (out.shape != q.shape or out.dtype != torch.bfloat16
+          or out.device != q.device or not out.is_contiguous()):
+        raise ValueError("out must be a contiguous bf16 tensor shaped like q")
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    elif (tuple(lse.shape) != (B, H, N) or lse.dtype != torch.float32
+          or lse.device != q.device or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous float32 tensor [B, H, N]")
+    with torch.cuda.device(q.device):
+        if stream is None:
+            stream = torch.cuda.current_stream(q.device)
+        handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+        rc = lib.attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                          lse.data_ptr(), B, H, N, d, float(scale), int(bool(causal)),
+                          handle)
+    if rc:
+        raise AttnError(rc, attn_strerror(rc))
+    return out, lse

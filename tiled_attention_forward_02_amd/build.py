@@ -1,0 +1,58 @@
+"""Build libmi_attn.so in-tree with hipcc for gfx950.
+
+Run as ``python -m tiled_attention_forward_02_amd.build`` or call build().
+The shared library lands next to this file, where the binding loads it.
+"""
+
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG_DIR)
+SRC = os.path.join(PKG_DIR, "csrc", "attn_fwd.hip")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG_DIR, "libmi_attn.so")
+ARCH = "gfx950"
+
+
+def hipcc():
+    for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build libmi_attn)")
+
+
+def compile_command(out=LIB, extra=()):
+    return [
+        hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+        # packed fp32 VALU forms are kept off: plain fp32 code only
+        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        "-Wall", "-Wno-unused-function",
+        "-I", INCLUDE, SRC, "-o", out, *extra,
+    ]
+
+
+def build(verbose=False):
+    """Compile the HIP source into libmi_attn.so (always recompiles)."""
+    tmp = LIB + ".tmp"
+    cmd = compile_command(out=tmp)
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    # hipcc's host pass does not know the packed-fp32 feature; that note is noise
+    noise = "is not a recognized feature for this target"
+    err = "\n".join(l for l in res.stderr.splitlines() if noise not in l)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
+    if verbose and err.strip():
+        print(err, file=sys.stderr)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))
