@@ -1,0 +1,252 @@
+"""Benchmark of the fused attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--no-cpu-baseline] [--copy-calibration MIB]
+
+A step is one attn_fwd call over the whole workload (every query row of every
+(batch, head)) with inputs already resident in HBM. The default workload is
+the non-causal d=128, N=4096 one (B=16, H=16) that the throughput target is
+quoted on. Prints ONE JSON line on stdout; diagnostics go to stderr.
+
+FLOP per step follow the metric: 4*B*H*N^2*d, halved when causal.
+roofline.achieved = FLOP per launch / average launch duration, the duration
+taken with HIP events on the stream the kernel is launched on. Peak is the
+MI355X dense bf16 MFMA figure, 2516.6 TFLOP/s (256 CU x 4096 FLOP/clk x 2.4
+GHz). roofline.traffic (HBM bytes per launch) comes from the rocprofv3
+FETCH_SIZE / WRITE_SIZE summary committed under profiles/, and is null when
+that summary was taken on a different kernel source.
+
+--copy-calibration MIB runs only a plain device-to-device copy of that many
+MiB (the known-size reference for the FETCH_SIZE / WRITE_SIZE counters) and
+prints its size as JSON.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6
+HBM_PEAK_GBS = 8000.0
+DEFAULT_WORKLOAD = "b16h16n4096d128"
+KERNEL_SRC = os.path.join(ROOT, "tiled_attention_forward_02_amd", "csrc", "attn_fwd.hip")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_sha():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def stored_traffic(workload):
+    """HBM bytes per launch from the committed counter summary, or None when
+    it is missing or was taken on another version of the kernel source."""
+    path = os.path.join(PROFILES, f"attn_fwd_{workload}_hbm_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            key, val = line.split(":", 1)
+            fields[key.strip()] = val.strip()
+    if fields.get("kernel_source_sha256_16") != kernel_sha():
+        return None
+    try:
+        return int(float(fields["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, inp, budget_s=15.0):
+    """Time the fp64 oracle on whole heads of the same workload until about
+    budget_s seconds of CPU work are done; report it in the metric's unit."""
+    import numpy as np
+    import torch
+
+    from oracle import attend_head
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    except Exception:  # threadpoolctl missing: numpy's BLAS threads unknown
+        threads = os.cpu_count() or 1
+    q, k, v = inp["q"], inp["k"], inp["v"]
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    done = 0
+    t0 = time.perf_counter()
+    for b, h in heads:
+        attend_head(q[b, h].to(torch.float64).numpy(), k[b, h].to(torch.float64).numpy(),
+                    v[b, h].to(torch.float64).numpy(), inp["scale"], w.causal)
+        done += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    flops = done * 4.0 * w.N * w.N * w.d / (2 if w.causal else 1)
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{done} of {len(heads)} heads (N={w.N}, d={w.d}, "
+                  f"causal={w.causal}) in {dt:.1f} s, numpy fp64, "
+                  f"metric FLOP of those heads / wall time",
+    }
+
+
+def parity_sample(w, inp, o, lse, rows=16):
+    """A quick sampled check against the oracle before timing."""
+    import numpy as np
+    import torch
+
+    from oracle import attend_head
+    rng = np.random.default_rng(7)
+    eo = el = 0.0
+    for b, h in ((0, 0), (w.B - 1, w.H - 1)):
+        r = np.sort(rng.choice(w.N, rows, replace=False))
+        o_ref, l_ref = attend_head(inp["q"][b, h][r].to(torch.float64).numpy(),
+                                   inp["k"][b, h].to(torch.float64).numpy(),
+                                   inp["v"][b, h].to(torch.float64).numpy(),
+                                   inp["scale"], w.causal, q_pos=r)
+        eo = max(eo, float(np.abs(o[b, h][r] - o_ref).max()))
+        el = max(el, float(np.abs(lse[b, h][r] - l_ref).max()))
+    return {"max_abs_dO": eo, "max_abs_dlse": el, "ok": eo <= 2e-2 and el <= 1e-3}
+
+
+def copy_calibration(mib):
+    import torch
+    n = mib * (1 << 20)
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the attention forward is built and "
+              "measured on a single MI355X (each head is independent; sharding "
+              "heads over GPUs needs no exchange). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import tiled_attention_forward_02_amd as mi
+    from tiled_attention_forward_02_amd.workloads import attn_flops, make_inputs, workload
+
+    if not torch.cuda.is_available():
+        log("no HIP device visible")
+        sys.exit(1)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
+
+    w = workload(args.workload)
+    dev = torch.device("cuda:0")
+    log(f"workload {w.name}: B={w.B} H={w.H} N={w.N} d={w.d} causal={w.causal}")
+    inp = make_inputs(w)
+    q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    shape = mi.attn_fwd_launch_shape(w.B, w.H, w.N, w.d, w.causal)
+    log(f"launch: {shape}")
+
+    def step():
+        mi.attn_fwd(q, k, v, scale=inp["scale"], causal=w.causal, out=o, lse=lse)
+
+    step()
+    torch.cuda.synchronize()
+    parity = parity_sample(w, inp, o.float().cpu().numpy(), lse.cpu().numpy())
+    log(f"parity sample: {parity}")
+    if not parity["ok"]:
+        log("parity check failed; refusing to report a throughput")
+        sys.exit(1)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    event_ms = ev0.elapsed_time(ev1)
+
+    flops = attn_flops(w.B, w.H, w.N, w.d, w.causal)
+    launch_s = event_ms / 1e3 / args.steps
+    achieved = flops / launch_s / 1e12
+    value = flops * args.steps / wall / 1e12
+    traffic = stored_traffic(w.name)
+    log(f"wall {wall*1e3:.2f} ms for {args.steps} steps; event avg {launch_s*1e6:.1f} us/launch")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the oracle on the host cores ...")
+        cpu = cpu_baseline(w, inp, args.cpu_budget)
+
+    line = {
+        "metric": "attention fwd TFLOP/s and % of MI355X bf16 MFMA peak at d=64/128",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": w.as_dict(),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
+        },
+        "cpu_baseline": cpu,
+        "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "kernel_avg_us": round(launch_s * 1e6, 2),
+        "parity_sample": parity,
+        "kernel_source_sha256_16": kernel_sha(),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

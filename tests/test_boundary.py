@@ -147,7 +147,7 @@ def test_launch_shape(lib, B, H, N, d, causal):
     bm = s["block_m"]
     assert s["grid"] == B * H * ((N + bm - 1) // bm)
     assert s["block"] % 64 == 0 and s["block"] <= 1024
-    assert s["block_n"] * d == 8192
+    assert s["block_n"] in (32, 64, 128)
     assert 0 < s["lds_bytes"] <= 160 * 1024
 
 

@@ -31,6 +31,8 @@ def compile_command(out=LIB, extra=()):
         hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
         # packed fp32 VALU forms are kept off: plain fp32 code only
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # NaN-free max/min on the device side only (no canonicalising moves)
+        "-Xarch_device", "-fno-honor-nans",
         "-Wall", "-Wno-unused-function",
         "-I", INCLUDE, SRC, "-o", out, *extra,
     ]

@@ -8,22 +8,31 @@
 // per-row log-sum-exp is written next to the output, as in the Triton forward
 // signature on that same page (Out, Lse, softmax_scale, IS_CAUSAL).
 //
-// Design for MI355X (gfx950): one workgroup of 4 waves owns 128 query rows of
-// one (batch, head); each wave owns 32 rows. Key/value tiles of 8192 elements
-// (64 keys at d=128, 128 keys at d=64) are streamed HBM -> registers -> LDS,
-// double buffered, one tile ahead. Both contractions run on
-// v_mfma_f32_32x32x16_bf16:
+// Design for MI355X (gfx950). One workgroup of 4 waves owns 128 query rows of
+// one (batch, head); each wave owns 32 rows, and two workgroups share a CU so
+// that each SIMD holds two waves whose softmax (VALU) and matrix (MFMA) phases
+// interleave. Keys and values stream through LDS in tiles of 64 keys, HBM ->
+// registers -> LDS, double buffered one tile ahead with one barrier per tile.
+// Global loads are buffer loads: rows past N come back as zeros, with no
+// branches. Both contractions run on v_mfma_f32_32x32x16_bf16 in transposed
+// form:
 //
 //   S^T (keys x queries) = K (keys x d) * Q^T (d x queries)
 //   O^T (d x queries)   += V^T (d x keys) * P^T (keys x queries)
 //
-// Computing the transposed products puts one query per lane (lane % 32) in
-// both accumulators, so the row statistics (max, sum, rescale) are per-lane
-// scalars plus one exchange between the two 32-lane halves, and the S^T
-// accumulator, rounded to bf16, is already the B operand of the P*V product
-// after a fixed permutation of the key order inside each 16-key slice. V^T is
-// written to LDS in that permuted order, so the A operand is one 16-byte LDS
-// read per lane.
+// so one query sits in each lane (lane % 32) of both accumulators: the row
+// statistics are per-lane scalars plus one swap between the two 32-lane
+// halves, and the S^T accumulator rounded to bf16 is already the B operand of
+// the P*V product, given a fixed permutation of the key order inside each
+// 16-key slice. V^T is written to LDS in that permuted order.
+//
+// The running maximum is raised lazily: only when a tile's row maximum
+// exceeds it by more than 2^8 (log2 units) are O and the row sum rescaled;
+// otherwise the stale maximum is kept, the weights of that tile are at most
+// 2^8, and O / l and m + log2(l) stay exact in real arithmetic because O and
+// l always share one reference maximum. Masking (causal diagonal tiles and
+// the tile holding key N-1) is the only per-element select, and only those
+// tiles run it.
 //
 // MFMA 32x32x16 fragment layout used below (lane l, h = l / 32, c = l % 32):
 //   A (32 x 16):  lane holds row c, k-elements 8h .. 8h+7
@@ -37,6 +46,10 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <string.h>
+
+#include <type_traits>
+
 #include "mi_attn.h"
 
 namespace {
@@ -46,45 +59,49 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kLazyMax = 8.0f;  // tolerated growth of the row max, log2 units
 
-constexpr int kWaves = 4;                 // waves per workgroup
-constexpr int kThreads = 64 * kWaves;     // threads per workgroup
-constexpr int kBlockM = 32 * kWaves;      // query rows per workgroup
+constexpr int kWaves = 4;              // waves per workgroup
+constexpr int kThreads = 64 * kWaves;  // threads per workgroup
+constexpr int kBlockM = 32 * kWaves;   // query rows per workgroup
+constexpr int kBlockN = 64;            // keys per tile
 
 // Per head dimension D: the key tile and its LDS layout.
 template <int D>
 struct Tile {
-  static constexpr int BN = 8192 / D;          // keys per step (64 or 128)
-  static constexpr int NKB = BN / 32;          // 32-key MFMA blocks per step
-  static constexpr int KSTRIDE = D + 8;        // K row pitch in LDS (bf16), 16 B pad
-  static constexpr int K_ELEMS = BN * KSTRIDE; // K tile
-  static constexpr int VT_ELEMS = D * BN;      // V^T tile
+  static constexpr int BN = kBlockN;
+  static constexpr int KS = D + 8;               // K row pitch in LDS (bf16), 16 B pad
+  static constexpr int K_ELEMS = BN * KS;        // one K tile
+  static constexpr int VT_ELEMS = D * BN;        // one V^T tile
+  static constexpr int CPR = D / 8;              // 16-byte chunks per row
+  static constexpr int KPT = BN * CPR / kThreads;  // rows each thread stages (4 or 2)
   static constexpr int STAGE = K_ELEMS + VT_ELEMS;
-  static constexpr int CPR = D / 8;            // 16-byte chunks per global row
-  static constexpr int LDS_BYTES = 2 * STAGE * 2;
-  static_assert(BN * CPR == 4 * kThreads, "each thread stages 4 chunks of K and of V");
+  static constexpr int LDS_ELEMS = 2 * STAGE;
+  static constexpr int LDS_BYTES = 2 * LDS_ELEMS;
+  static_assert(KPT == 2 || KPT == 4, "staging layout");
 };
 
 // Key order inside a 16-key slice of V^T in LDS: swaps bits 2 and 3 of the
 // key offset, matching where the S^T accumulator leaves each key (C layout
-// row 8*(i/4) + 4h + i%4 read as B-operand element 8h + j).
+// row 8*(i/4) + 4h + i%4 read as B-operand element 8h + j). Its own inverse.
 __device__ __forceinline__ int slice_pos(int o) {
   return (o & 3) | ((o & 4) << 1) | ((o & 8) >> 1);
 }
 
-// XOR swizzle of 16-byte blocks inside a V^T row, so that the 8 rows read by
-// 8 consecutive lanes land in 8 different blocks (distinct banks) and the
-// transposing writes spread over blocks too.
-__device__ __forceinline__ int vt_swz(int d) { return (d ^ (d >> 3)) & 7; }
+// XOR swizzle of the 16-byte blocks of a V^T row, a function of d mod 32 only
+// (so it is the same for every 32-row block a lane reads): any 8 aligned
+// consecutive rows, and any 16, land on distinct blocks / bank groups.
+__device__ __forceinline__ int vt_swz(int d) { return ((d & 31) ^ ((d & 31) >> 3)) & 7; }
 
 // Workgroup id -> (batch*head, query tile). Workgroups are dealt to the 8
 // XCDs round-robin, so when B*H is a multiple of 8 each XCD gets the heads
 // h = x (mod 8) and walks them head by head (non-causal: the q-tiles of one
 // head run together and share that XCD's L2 for K and V) or q-tile by q-tile
-// from the heaviest (causal: longest key prefix first, so short tiles fill the
+// from the heaviest (causal: longest key prefix first, short tiles fill the
 // tail).
 __device__ __forceinline__ void map_block(int bid, int BH, int nq, bool causal,
                                           int& bh, int& qt) {
@@ -106,10 +123,28 @@ __device__ __forceinline__ void map_block(int bid, int BH, int nq, bool causal,
   }
 }
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  const __bf16 a = (__bf16)lo, b = (__bf16)hi;  // round to nearest even
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) |
-         ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+// Buffer resource over [base, base + bytes): loads past the end return 0 and
+// stores past the end are dropped by the hardware range check.
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+__device__ __forceinline__ u32x4 load16(rsrc_t r, uint32_t byte_off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 0);
+}
+
+// Value of x in the lane 32 positions away, combined with op (same result in
+// both lanes of the pair, bit for bit).
+__device__ __forceinline__ float swap_halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float swap_halves_add(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 template <int D, bool CAUSAL>
@@ -118,8 +153,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
     const __bf16* __restrict__ V, __bf16* __restrict__ O,
     float* __restrict__ LSE, int BH, int N, int nq, float c) {
   using T = Tile<D>;
-  constexpr int BN = T::BN, NKB = T::NKB, KS = T::KSTRIDE, CPR = T::CPR;
-  __shared__ __attribute__((aligned(16))) __bf16 smem[2 * T::STAGE];
+  constexpr int BN = T::BN, KS = T::KS, CPR = T::CPR, KPT = T::KPT;
+  __shared__ __attribute__((aligned(16))) __bf16 smem[T::LDS_ELEMS];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, col = lane & 31, half = lane >> 5;
@@ -131,197 +166,211 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
   const int qi = qw + col;        // this lane's query row
 
   const size_t head = (size_t)bh * (size_t)N * D;
-  const __bf16* Qh = Q + head;
-  const __bf16* Kh = K + head;
-  const __bf16* Vh = V + head;
+  const uint32_t head_bytes = (uint32_t)N * D * 2;
+  const rsrc_t rq = make_rsrc(Q + head, head_bytes);
+  const rsrc_t rk = make_rsrc(K + head, head_bytes);
+  const rsrc_t rv = make_rsrc(V + head, head_bytes);
 
-  // Q^T fragments (B operand): lane holds Q[qi][16s + 8h .. +7] for s < D/16.
+  // Q^T fragments (B operand): lane holds Q[qi][16s + 8h .. +7]; zero past N.
+  u32x4 qraw[D / 16];
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s)
+    qraw[s] = load16(rq, (uint32_t)(qi * D + 16 * s + 8 * half) * 2);
+  // Fold the sign of the scale into Q (exact) so that c > 0 below: then a
+  // masked score of -inf gets weight exp2(-inf) = 0 and the row max skips it.
+  // scale == 0 makes every score 0, the same as Q == 0 with any scale.
+  if (c < 0.f) {
+    c = -c;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) qraw[s] ^= 0x80008000u;
+  } else if (c == 0.f) {
+    c = 1.f;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) qraw[s] = u32x4{0, 0, 0, 0};
+  }
   bf16x8 qf[D / 16];
 #pragma unroll
-  for (int s = 0; s < D / 16; ++s) {
-    if (qi < N) {
-      qf[s] = *reinterpret_cast<const bf16x8*>(Qh + (size_t)qi * D + 16 * s + 8 * half);
-    } else {
-      qf[s] = bf16x8{};
-    }
-  }
+  for (int s = 0; s < D / 16; ++s) qf[s] = __builtin_bit_cast(bf16x8, qraw[s]);
 
   // Keys this workgroup / this wave can see.
   const int kv_end = CAUSAL ? min(N, q0 + kBlockM) : N;
+  const int nt = (kv_end + BN - 1) / BN;
   const int wave_kv_end = CAUSAL ? min(N, qw + 32) : N;
-  const int ntiles = (kv_end + BN - 1) / BN;
 
-  // Staging: thread owns rows kr .. kr+3 of the tile, 16-byte chunk dc.
-  const int kr = 4 * (tid / CPR);
-  const int dc = tid % CPR;
-  u32x4 kreg[4], vreg[4];
+  // Staging. K: thread owns rows kr_k .. +KPT-1, 16-byte chunk dc_k, with the
+  // chunk fastest across lanes (whole rows per 16 lanes: coalesced loads,
+  // contiguous LDS writes). V: the key group fastest across lanes, so the 16
+  // lanes of one transposed LDS write cover 16 different key groups of one
+  // column (distinct banks) and each load still reads 64 contiguous bytes.
+  const int kr_k = KPT * (tid / CPR);
+  const int dc_k = tid % CPR;
+  const int kr_v = KPT * (tid % 16) + 16 * KPT * (tid / (16 * CPR));
+  const int dc_v = (tid / 16) % CPR;
+  const uint32_t koff = (uint32_t)(kr_k * D + 8 * dc_k) * 2;
+  const uint32_t voff = (uint32_t)(kr_v * D + 8 * dc_v) * 2;
+  u32x4 kst[KPT], vst[KPT];
 
-  auto load_tile = [&](int k0) {
+  auto gload = [&](int k0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = k0 + kr + i;
-      if (row < N) {
-        const size_t off = (size_t)row * D + 8 * dc;
-        kreg[i] = *reinterpret_cast<const u32x4*>(Kh + off);
-        vreg[i] = *reinterpret_cast<const u32x4*>(Vh + off);
-      } else {  // past the end: zeros (their weight is 0, and 0 * 0 stays finite)
-        kreg[i] = u32x4{0, 0, 0, 0};
-        vreg[i] = u32x4{0, 0, 0, 0};
-      }
+    for (int i = 0; i < KPT; ++i) {
+      const uint32_t row = (uint32_t)((k0 + i) * D * 2);
+      kst[i] = load16(rk, koff + row);
+      vst[i] = load16(rv, voff + row);
     }
   };
-
-  auto store_tile = [&](int stage) {
-    __bf16* Ks = smem + stage * T::STAGE;
-    __bf16* Vts = Ks + T::K_ELEMS;
+  // Per-lane LDS byte offsets that do not change with the tile.
+  const uint32_t k_wr = (uint32_t)(kr_k * KS + 8 * dc_k) * 2;
+  const int vpos = 16 * (kr_v >> 4) + slice_pos(kr_v & 15);
+  uint32_t v_wr[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      *reinterpret_cast<u32x4*>(Ks + (kr + i) * KS + 8 * dc) = kreg[i];
-    }
-    // V^T: for each of the chunk's 8 columns d, the 4 keys kr..kr+3 are
-    // contiguous in the permuted slice order -> one 8-byte write per column.
-    const int pos = 16 * (kr >> 4) + slice_pos(kr & 15);
+  for (int e = 0; e < 8; ++e) {
+    const int d = 8 * dc_v + e;
+    v_wr[e] = (uint32_t)(T::K_ELEMS + d * BN + ((vpos >> 3) ^ vt_swz(d)) * 8 + (vpos & 7)) * 2;
+  }
+  const uint32_t k_rd = (uint32_t)(col * KS + 8 * half) * 2;
+  uint32_t v_rd[4];  // V^T read of 16-key slice g for rows 32*db + col (db added as immediate)
+#pragma unroll
+  for (int g = 0; g < 4; ++g)
+    v_rd[g] = (uint32_t)(T::K_ELEMS + col * BN + ((2 * g + half) ^ vt_swz(col)) * 8) * 2;
+
+  char* const lds = reinterpret_cast<char*>(smem);
+  // K rows as they are; V^T with, for each of the chunk's 8 columns d, the KPT
+  // keys kr_v.. contiguous in the permuted slice order -> one write per column.
+  auto lds_store = [&](auto stage_c) {
+    constexpr uint32_t base = decltype(stage_c)::value * T::STAGE * 2;
+#pragma unroll
+    for (int i = 0; i < KPT; ++i)
+      *reinterpret_cast<u32x4*>(lds + base + k_wr + i * KS * 2) = kst[i];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int w = e >> 1;
-      uint32_t lo, hi;
-      if (e & 1) {
-        lo = (vreg[0][w] >> 16) | (vreg[1][w] & 0xffff0000u);
-        hi = (vreg[2][w] >> 16) | (vreg[3][w] & 0xffff0000u);
+      // bytes of the bf16 at even (0x05040100) or odd (0x07060302) column e
+      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+      const uint32_t lo = __builtin_amdgcn_perm(vst[1][w], vst[0][w], sel);
+      if constexpr (KPT == 4) {
+        const uint32_t hi = __builtin_amdgcn_perm(vst[3][w], vst[2][w], sel);
+        *reinterpret_cast<u32x2*>(lds + base + v_wr[e]) = u32x2{lo, hi};
       } else {
-        lo = (vreg[0][w] & 0xffffu) | (vreg[1][w] << 16);
-        hi = (vreg[2][w] & 0xffffu) | (vreg[3][w] << 16);
+        *reinterpret_cast<uint32_t*>(lds + base + v_wr[e]) = lo;
       }
-      const int d = 8 * dc + e;
-      const int blk = (pos >> 3) ^ vt_swz(d);
-      *reinterpret_cast<u32x2*>(Vts + d * BN + blk * 8 + (pos & 7)) = u32x2{lo, hi};
     }
   };
 
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
-  float run_max = -INFINITY;  // in log2 units: max of s * scale * log2(e)
-  float run_sum = 0.f;        // this lane's share of the row sum
+  float m_run = -INFINITY;  // reference maximum of O and l, log2 units
+  float l_run = 0.f;        // this lane's share of the row sum
 
-  const bool pos_scale = c >= 0.f;
-  const float mask_val = pos_scale ? -INFINITY : INFINITY;
-
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-
-  for (int t = 0; t < ntiles; ++t) {
+  // One tile: S^T, mask, running max, P, O^T += V^T P^T; then stage the next.
+  auto step = [&](int t, auto stage_c) {
+    constexpr int stage = decltype(stage_c)::value;
+    constexpr uint32_t base = stage * T::STAGE * 2;
     const int k0 = t * BN;
-    if (t + 1 < ntiles) load_tile(k0 + BN);
+    const bool has_next = t + 1 < nt;
+    if (has_next) gload(k0 + BN);
 
     if (k0 < wave_kv_end) {
-      const __bf16* Ks = smem + (t & 1) * T::STAGE;
-      const __bf16* Vts = Ks + T::K_ELEMS;
-
-      // S^T = K * Q^T for the tile's NKB blocks of 32 keys.
-      f32x16 sacc[NKB];
+      // S^T = K * Q^T: two blocks of 32 keys.
+      f32x16 sacc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) sacc[kb] = f32x16{};
+      for (int j = 0; j < D / 16; ++j) {
 #pragma unroll
-      for (int s = 0; s < D / 16; ++s) {
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
+        for (int kb = 0; kb < 2; ++kb) {
           const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-              Ks + (32 * kb + col) * KS + 16 * s + 8 * half);
-          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sacc[kb], 0, 0, 0);
+              lds + base + k_rd + (32 * kb * KS + 16 * j) * 2);
+          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[j], sacc[kb], 0, 0, 0);
         }
       }
 
-      // Hide keys past the end and (causal) keys after the query.
-      const bool need_mask = (k0 + BN > N) || (CAUSAL && k0 + BN - 1 > qw);
-      if (need_mask) {
+      // Keys past the end and (causal) keys after the query get -inf.
+      if ((k0 + BN > N) || (CAUSAL && k0 + BN - 1 > qw)) {
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int key = k0 + 32 * kb + 8 * (i >> 2) + 4 * half + (i & 3);
-            const bool vis = key < N && (!CAUSAL || key <= qi);
-            if (!vis) sacc[kb][i] = mask_val;
+            if (key >= N || (CAUSAL && key > qi)) sacc[kb][i] = -INFINITY;
           }
-        }
       }
 
-      // Row extreme of the raw scores (max if the scale is >= 0, else min),
-      // combined across the two lane halves that share the query.
-      float ext = sacc[0][0];
-      if (pos_scale) {
+      // Row maximum of the tile in log2 units, both halves combined.
+      float mx = fmaxf(sacc[0][0], sacc[1][0]);
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) ext = fmaxf(ext, sacc[kb][i]);
-        ext = fmaxf(ext, __shfl_xor(ext, 32));
-      } else {
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) ext = fminf(ext, sacc[kb][i]);
-        ext = fminf(ext, __shfl_xor(ext, 32));
-      }
-      // fmaxf ignores a NaN from 0 * inf (scale 0, row fully masked here).
-      const float new_max = fmaxf(run_max, ext * c);
-      const float alpha = __builtin_amdgcn_exp2f(run_max - new_max);
+      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(sacc[0][i], sacc[1][i]));
+      const float m_tile = swap_halves_max(mx) * c;
 
-      // p = 2^(s*c - m): the exp of the scaled, max-subtracted score.
-      float tile_sum = 0.f;
-      bf16x8 pb[NKB][2];
+      // Raise the reference maximum only when the tile's exceeds it by more
+      // than kLazyMax (always on the first tile, where m_run = -inf).
+      if (__any(m_tile > m_run + kLazyMax)) {
+        const float m_new = fmaxf(m_run, m_tile);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        l_run *= alpha;
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
+        for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
+        m_run = m_new;
+      }
+
+      // P = 2^(s*c - m_run), rounded to bf16; the row sum in fp32.
+      bf16x8 pb[2][2];
+      float tsum = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          float p = __builtin_amdgcn_exp2f(fmaf(sacc[kb][i], c, -new_max));
-          if (need_mask && sacc[kb][i] == mask_val) p = 0.f;
-          tile_sum += p;
+          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kb][i], c, -m_run));
+          tsum += p;
           pb[kb][i >> 3][i & 7] = (__bf16)p;
         }
-      }
-      run_sum = run_sum * alpha + tile_sum;
-      run_max = new_max;
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
+      l_run += tsum;
 
       // O^T += V^T * P^T, 16 keys per MFMA.
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int sg = 0; sg < 2; ++sg) {
-          const int g = 2 * kb + sg;  // 16-key slice index in the tile
 #pragma unroll
           for (int db = 0; db < D / 32; ++db) {
-            const int d = 32 * db + col;
-            const int blk = (2 * g + half) ^ vt_swz(d);
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(Vts + d * BN + blk * 8);
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+                lds + base + v_rd[2 * kb + sg] + 32 * db * BN * 2);
             oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kb][sg], oacc[db], 0, 0, 0);
           }
         }
-      }
     }
 
-    if (t + 1 < ntiles) store_tile((t + 1) & 1);
+    if (has_next) lds_store(std::integral_constant<int, stage ^ 1>{});
     __syncthreads();
+  };
+
+  gload(0);
+  lds_store(std::integral_constant<int, 0>{});
+  __syncthreads();
+  for (int t = 0; t < nt; t += 2) {
+    step(t, std::integral_constant<int, 0>{});
+    if (t + 1 < nt) step(t + 1, std::integral_constant<int, 1>{});
   }
 
-  // Epilogue: O = acc / l (bf16), lse = (m + log2 l) * ln 2.
-  const float total = run_sum + __shfl_xor(run_sum, 32);
-  if (qi < N) {
-    const float inv = 1.0f / total;
-    __bf16* Orow = O + head + (size_t)qi * D;
+  // Epilogue: O = acc / l (bf16), lse = (m + log2 l) * ln 2. Rows past N are
+  // dropped by the buffer range check.
+  const float total = swap_halves_add(l_run);
+  const float inv = 1.0f / total;
+  const rsrc_t ro = make_rsrc(O + head, head_bytes);
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
+  for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        bf16x4 v4;
+    for (int r = 0; r < 4; ++r) {
+      bf16x4 v4;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v4[e] = (__bf16)(oacc[db][4 * r + e] * inv);
-        *reinterpret_cast<bf16x4*>(Orow + 32 * db + 8 * r + 4 * half) = v4;
-      }
+      for (int e = 0; e < 4; ++e) v4[e] = (__bf16)(oacc[db][4 * r + e] * inv);
+      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v4), ro,
+                                            (int)((qi * D + 32 * db + 8 * r + 4 * half) * 2),
+                                            0, 0);
     }
-    if (half == 0) LSE[(size_t)bh * N + qi] = (run_max + log2f(total)) * kLn2;
+  }
+  if (half == 0) {
+    const rsrc_t rl = make_rsrc(LSE + (size_t)bh * N, (uint32_t)N * 4);
+    const float lse = (m_run + log2f(total)) * kLn2;
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lse), rl, qi * 4, 0, 0);
   }
 }
 
@@ -334,8 +383,8 @@ struct Shape {
 int check_sizes(int B, int H, int N, int d, Shape* sh) {
   if (B < 0 || H < 0 || N < 0) return ATTN_ERR_SHAPE;
   if (d != 64 && d != 128) return ATTN_ERR_HEADDIM;
-  const int64_t rows = (int64_t)B * H * N;
-  if (rows > 0 && rows > INT64_MAX / d) return ATTN_ERR_SHAPE;
+  // One head's tensor is addressed with 32-bit byte offsets.
+  if ((int64_t)N * d * 2 + (int64_t)kBlockM * d * 2 > INT32_MAX) return ATTN_ERR_SHAPE;
   if ((int64_t)B * H > INT32_MAX) return ATTN_ERR_SHAPE;
   const int64_t nq = ((int64_t)N + kBlockM - 1) / kBlockM;
   const int64_t grid = (int64_t)B * H * nq;
@@ -344,7 +393,7 @@ int check_sizes(int B, int H, int N, int d, Shape* sh) {
   sh->block = kThreads;
   sh->lds = d == 64 ? Tile<64>::LDS_BYTES : Tile<128>::LDS_BYTES;
   sh->block_m = kBlockM;
-  sh->block_n = d == 64 ? Tile<64>::BN : Tile<128>::BN;
+  sh->block_n = kBlockN;
   sh->nq = (int)nq;
   return ATTN_OK;
 }
@@ -375,7 +424,9 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, fl
   Shape sh;
   const int rc = check_sizes(B, H, N, d, &sh);
   if (rc != ATTN_OK) return rc;
-  if (!isfinite(scale)) return ATTN_ERR_SCALE;
+  uint32_t sbits;
+  memcpy(&sbits, &scale, 4);
+  if ((sbits & 0x7f800000u) == 0x7f800000u) return ATTN_ERR_SCALE;  // NaN or +-inf
   if (sh.grid == 0) return ATTN_OK;  // B*H*N == 0: nothing to compute
   if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL;
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15) return ATTN_ERR_ALIGN;
