@@ -63,7 +63,8 @@ typedef enum {
  *
  * Errors: arguments are validated before any HIP call. On a validation error
  * nothing is launched and o, lse are untouched. ATTN_ERR_LAUNCH reports the
- * status of the launch itself. NaN or Inf inside q, k, v propagate.
+ * status of the launch itself. With NaN or Inf inside q, k or v the outputs
+ * are unspecified.
  */
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              int B, int H, int N, int d, float scale, int causal, void* stream);
