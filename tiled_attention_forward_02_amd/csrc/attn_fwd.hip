@@ -9,9 +9,10 @@
 // signature on that same page (Out, Lse, softmax_scale, IS_CAUSAL).
 //
 // Design for MI355X (gfx950). One workgroup of 4 waves owns 128 query rows of
-// one (batch, head); each wave owns 32 rows, and two workgroups share a CU so
-// that each SIMD holds two waves whose softmax (VALU) and matrix (MFMA) phases
-// interleave. Keys and values stream through LDS in tiles of 64 keys, HBM ->
+// one (batch, head); each wave owns 32 rows, and three (d=128) or four (d=64)
+// workgroups share a CU, so each SIMD holds waves of different workgroups
+// whose softmax (VALU) and matrix (MFMA) phases interleave. Keys and values
+// stream through LDS in tiles of 32 (d=128) or 64 (d=64) keys, HBM ->
 // registers -> LDS, double buffered one tile ahead with one barrier per tile.
 // Global loads are buffer loads: rows past N come back as zeros, with no
 // branches. Both contractions run on v_mfma_f32_32x32x16_bf16 in transposed
@@ -68,12 +69,19 @@ constexpr float kLazyMax = 8.0f;  // tolerated growth of the row max, log2 units
 constexpr int kWaves = 4;              // waves per workgroup
 constexpr int kThreads = 64 * kWaves;  // threads per workgroup
 constexpr int kBlockM = 32 * kWaves;   // query rows per workgroup
-constexpr int kBlockN = 64;            // keys per tile
-
-// Per head dimension D: the key tile and its LDS layout.
+// Keys per tile for head dimension D. At d=128 a 32-key tile keeps a wave
+// under 168 VGPRs and a workgroup at 33 KiB of LDS, so three workgroups
+// (three waves per SIMD) share a CU; at d=64 a 64-key tile already fits four.
 template <int D>
+constexpr int kBlockN = 64;
+template <>
+constexpr int kBlockN<128> = 32;
+
+// Per head dimension D and tile width BN: the key tile and its LDS layout.
+template <int D, int BN_>
 struct Tile {
-  static constexpr int BN = kBlockN;
+  static constexpr int BN = BN_;
+  static constexpr int NKB = BN / 32;            // 32-key MFMA blocks per tile
   static constexpr int KS = D + 8;               // K row pitch in LDS (bf16), 16 B pad
   static constexpr int K_ELEMS = BN * KS;        // one K tile
   static constexpr int VT_ELEMS = D * BN;        // one V^T tile
@@ -92,10 +100,15 @@ __device__ __forceinline__ int slice_pos(int o) {
   return (o & 3) | ((o & 4) << 1) | ((o & 8) >> 1);
 }
 
-// XOR swizzle of the 16-byte blocks of a V^T row, a function of d mod 32 only
-// (so it is the same for every 32-row block a lane reads): any 8 aligned
-// consecutive rows, and any 16, land on distinct blocks / bank groups.
-__device__ __forceinline__ int vt_swz(int d) { return ((d & 31) ^ ((d & 31) >> 3)) & 7; }
+// XOR swizzle of the 16-byte blocks of a V^T row (BN/8 blocks), a function of
+// d mod 32 only (the same for every 32-row block a lane reads): any 8 aligned
+// consecutive rows, and any 16, land on distinct bank groups, whether a row
+// is 128 bytes (BN = 64) or 64 bytes (BN = 32).
+template <int BN>
+__device__ __forceinline__ int vt_swz(int d) {
+  d &= 31;
+  return BN == 64 ? ((d ^ (d >> 3)) & 7) : (((d >> 1) ^ (d >> 3)) & 3);
+}
 
 // Workgroup id -> (batch*head, query tile). Workgroups are dealt to the 8
 // XCDs round-robin, so when B*H is a multiple of 8 each XCD gets the heads
@@ -148,12 +161,12 @@ __device__ __forceinline__ float swap_halves_add(float x) {
 }
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
+__global__ __launch_bounds__(kThreads, kBlockN<D> == 32 ? 3 : 2) void attn_fwd_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     const __bf16* __restrict__ V, __bf16* __restrict__ O,
     float* __restrict__ LSE, int BH, int N, int nq, float c) {
-  using T = Tile<D>;
-  constexpr int BN = T::BN, KS = T::KS, CPR = T::CPR, KPT = T::KPT;
+  using T = Tile<D, kBlockN<D>>;
+  constexpr int BN = T::BN, KS = T::KS, CPR = T::CPR, KPT = T::KPT, NKB = T::NKB;
   __shared__ __attribute__((aligned(16))) __bf16 smem[T::LDS_ELEMS];
 
   const int tid = threadIdx.x;
@@ -225,13 +238,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const int d = 8 * dc_v + e;
-    v_wr[e] = (uint32_t)(T::K_ELEMS + d * BN + ((vpos >> 3) ^ vt_swz(d)) * 8 + (vpos & 7)) * 2;
+    v_wr[e] = (uint32_t)(T::K_ELEMS + d * BN + ((vpos >> 3) ^ vt_swz<BN>(d)) * 8 + (vpos & 7)) * 2;
   }
   const uint32_t k_rd = (uint32_t)(col * KS + 8 * half) * 2;
-  uint32_t v_rd[4];  // V^T read of 16-key slice g for rows 32*db + col (db added as immediate)
+  uint32_t v_rd[BN / 16];  // V^T read of 16-key slice g, rows 32*db + col (db: immediate)
 #pragma unroll
-  for (int g = 0; g < 4; ++g)
-    v_rd[g] = (uint32_t)(T::K_ELEMS + col * BN + ((2 * g + half) ^ vt_swz(col)) * 8) * 2;
+  for (int g = 0; g < BN / 16; ++g)
+    v_rd[g] = (uint32_t)(T::K_ELEMS + col * BN + ((2 * g + half) ^ vt_swz<BN>(col)) * 8) * 2;
 
   char* const lds = reinterpret_cast<char*>(smem);
   // K rows as they are; V^T with, for each of the chunk's 8 columns d, the KPT
@@ -271,12 +284,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
     if (has_next) gload(k0 + BN);
 
     if (k0 < wave_kv_end) {
-      // S^T = K * Q^T: two blocks of 32 keys.
-      f32x16 sacc[2] = {f32x16{}, f32x16{}};
+      // S^T = K * Q^T: NKB blocks of 32 keys, one MFMA chain each.
+      f32x16 sacc[NKB];
 #pragma unroll
-      for (int j = 0; j < D / 16; ++j) {
+      for (int kb = 0; kb < NKB; ++kb) {
+        sacc[kb] = f32x16{};
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int j = 0; j < D / 16; ++j) {
           const bf16x8 a = *reinterpret_cast<const bf16x8*>(
               lds + base + k_rd + (32 * kb * KS + 16 * j) * 2);
           sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[j], sacc[kb], 0, 0, 0);
@@ -286,7 +300,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
       // Keys past the end and (causal) keys after the query get -inf.
       if ((k0 + BN > N) || (CAUSAL && k0 + BN - 1 > qw)) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int key = k0 + 32 * kb + 8 * (i >> 2) + 4 * half + (i & 3);
@@ -295,9 +309,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
       }
 
       // Row maximum of the tile in log2 units, both halves combined.
-      float mx = fmaxf(sacc[0][0], sacc[1][0]);
+      float mx = fmaxf(sacc[0][0], sacc[0][1]);
 #pragma unroll
-      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(sacc[0][i], sacc[1][i]));
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int i = kb ? 0 : 2; i < 16; i += 2) mx = fmaxf(mx, fmaxf(sacc[kb][i], sacc[kb][i + 1]));
       const float m_tile = swap_halves_max(mx) * c;
 
       // Raise the reference maximum only when the tile's exceeds it by more
@@ -312,10 +328,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
       }
 
       // P = 2^(s*c - m_run), rounded to bf16; the row sum in fp32.
-      bf16x8 pb[2][2];
+      bf16x8 pb[NKB][2];
       float tsum = 0.f;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kb][i], c, -m_run));
@@ -326,7 +342,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
 
       // O^T += V^T * P^T, 16 keys per MFMA.
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int sg = 0; sg < 2; ++sg) {
 #pragma unroll
@@ -391,9 +407,9 @@ int check_sizes(int B, int H, int N, int d, Shape* sh) {
   if (grid > INT32_MAX) return ATTN_ERR_SHAPE;
   sh->grid = (int)grid;
   sh->block = kThreads;
-  sh->lds = d == 64 ? Tile<64>::LDS_BYTES : Tile<128>::LDS_BYTES;
+  sh->lds = d == 64 ? Tile<64, kBlockN<64>>::LDS_BYTES : Tile<128, kBlockN<128>>::LDS_BYTES;
   sh->block_m = kBlockM;
-  sh->block_n = kBlockN;
+  sh->block_n = d == 64 ? kBlockN<64> : kBlockN<128>;
   sh->nq = (int)nq;
   return ATTN_OK;
 }
