@@ -65,6 +65,12 @@ typedef __amdgpu_buffer_rsrc_t rsrc_t;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLazyMax = 8.0f;  // tolerated growth of the row max, log2 units
+constexpr float kLazySum = 4096.f;  // largest per-lane tile sum kept on a stale max
+// Softmax weights first, row maximum only when they grow too large (d=128,
+// where the 32-key tile's scores are cheap to keep live) or row maximum
+// first (d=64, where keeping 64 scores live would cost a wave per SIMD).
+template <int D>
+constexpr bool kSpeculativeWeights = D == 128;
 
 constexpr int kWaves = 4;              // waves per workgroup
 constexpr int kThreads = 64 * kWaves;  // threads per workgroup
@@ -308,36 +314,56 @@ __global__ __launch_bounds__(kThreads, kBlockN<D> == 32 ? 3 : 2) void attn_fwd_k
           }
       }
 
-      // Row maximum of the tile in log2 units, both halves combined.
-      float mx = fmaxf(sacc[0][0], sacc[0][1]);
+      // P = 2^(s*c - m_run), rounded to bf16, and its row sum (fp32).
+      bf16x8 pb[NKB][2];
+      float tsum = 0.f;
+      auto weights = [&]() __attribute__((always_inline)) {
+        tsum = 0.f;
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
+        for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int i = kb ? 0 : 2; i < 16; i += 2) mx = fmaxf(mx, fmaxf(sacc[kb][i], sacc[kb][i + 1]));
-      const float m_tile = swap_halves_max(mx) * c;
-
-      // Raise the reference maximum only when the tile's exceeds it by more
-      // than kLazyMax (always on the first tile, where m_run = -inf).
-      if (__any(m_tile > m_run + kLazyMax)) {
-        const float m_new = fmaxf(m_run, m_tile);
+          for (int i = 0; i < 16; ++i) {
+            const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kb][i], c, -m_run));
+            tsum += p;
+            pb[kb][i >> 3][i & 7] = (__bf16)p;
+          }
+      };
+      // Row maximum of the tile in log2 units, both lane halves combined.
+      auto tile_max = [&]() __attribute__((always_inline)) {
+        float mx = fmaxf(sacc[0][0], sacc[0][1]);
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int i = kb ? 0 : 2; i < 16; i += 2)
+            mx = fmaxf(mx, fmaxf(sacc[kb][i], sacc[kb][i + 1]));
+        return swap_halves_max(mx) * c;
+      };
+      // Move O and l to a new reference maximum.
+      auto rebase = [&](float m_new) __attribute__((always_inline)) {
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
         l_run *= alpha;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
         m_run = m_new;
-      }
-
-      // P = 2^(s*c - m_run), rounded to bf16; the row sum in fp32.
-      bf16x8 pb[NKB][2];
-      float tsum = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kb][i], c, -m_run));
-          tsum += p;
-          pb[kb][i >> 3][i & 7] = (__bf16)p;
+      };
+      if constexpr (kSpeculativeWeights<D>) {
+        // Weights against the current reference, without the tile's own
+        // maximum. The reference moves only when this lane's share of the
+        // tile's weights exceeds kLazySum (every weight then stayed below
+        // it), and always on the first tile, where m_run = -inf: the tile's
+        // true row maximum becomes the reference and the weights are redone.
+        weights();
+        if (t == 0 || __any(tsum > kLazySum)) {
+          rebase(fmaxf(m_run, tile_max()));
+          weights();
         }
+      } else {
+        // Move the reference only when the tile's row maximum exceeds it by
+        // more than kLazyMax (always on the first tile).
+        const float m_tile = tile_max();
+        if (__any(m_tile > m_run + kLazyMax)) rebase(fmaxf(m_run, m_tile));
+        weights();
+      }
       l_run += tsum;
 
       // O^T += V^T * P^T, 16 keys per MFMA.
@@ -408,8 +434,8 @@ int check_sizes(int B, int H, int N, int d, Shape* sh) {
   sh->grid = (int)grid;
   sh->block = kThreads;
   sh->lds = d == 64 ? Tile<64, kBlockN<64>>::LDS_BYTES : Tile<128, kBlockN<128>>::LDS_BYTES;
-  sh->block_m = kBlockM;
   sh->block_n = d == 64 ? kBlockN<64> : kBlockN<128>;
+  sh->block_m = kBlockM;
   sh->nq = (int)nq;
   return ATTN_OK;
 }
