@@ -29,7 +29,7 @@ extern "C" {
 typedef enum {
   ATTN_OK = 0,
   ATTN_ERR_NULL = -1,      /* a required pointer (q, k, v, o, lse, or an out-param) is NULL */
-  ATTN_ERR_SHAPE = -2,     /* B, H or N negative, or B*H*N*d overflows int64 / the grid */
+  ATTN_ERR_SHAPE = -2,     /* a size is negative, or one head (N*d*2 bytes) reaches 2^31 */
   ATTN_ERR_HEADDIM = -3,   /* d is neither 64 nor 128 */
   ATTN_ERR_ALIGN = -5,     /* q, k, v or o not 16-byte aligned, or lse not 4-byte aligned */
   ATTN_ERR_ALIAS = -6,     /* o or lse overlaps an input, or o overlaps lse */
@@ -68,6 +68,25 @@ typedef enum {
  */
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              int B, int H, int N, int d, float scale, int causal, void* stream);
+
+/*
+ * attn_fwd_cross - attention forward with Nq queries against Nk keys.
+ *
+ * The same operation as attn_fwd where queries and keys have their own
+ * lengths (cross attention, or a block of new queries against a longer key
+ * history). Shapes: q and o [B, H, Nq, d], k and v [B, H, Nk, d], lse
+ * [B, H, Nq]; layouts, dtypes, scale, stream, ownership and errors as for
+ * attn_fwd, with attn_fwd(..., N, ...) == attn_fwd_cross(..., N, N, ...).
+ *
+ * causal != 0 aligns the two axes at their ends: query i sits at position
+ * i + (Nk - Nq) on the key axis and sees keys j <= i + (Nk - Nq). When
+ * Nq > Nk the first Nq - Nk queries therefore see no key; such a row (and
+ * every row when Nk == 0) gets o = 0 and lse = -inf. k and v may be NULL when
+ * Nk == 0. If B*H*Nq == 0 the call does nothing and returns ATTN_OK.
+ */
+int attn_fwd_cross(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                   void* stream);
 
 /* attn_strerror - static, NUL-terminated description of a status code
  * (an unknown code yields "unknown status"). Never NULL. */

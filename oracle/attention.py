@@ -21,7 +21,10 @@ Readings taken where the pages are silent (each is listed in the design notes):
 
 * ``scale`` multiplies Q K^T before masking and softmax.
 * causal: key j is visible to query i iff j <= i (queries and keys share one
-  position axis); masked keys get weight exactly 0.
+  position axis); masked keys get weight exactly 0. With M queries and N keys
+  (M != N) the two axes are aligned at their ends: query i sits at position
+  i + (N - M) on the key axis. A query that then sees no key at all gets
+  o = 0 and lse = -inf (the empty sum).
 * lse is the natural log of sum_j exp(s_ij) over the visible keys, using the
   scaled scores.
 
@@ -42,9 +45,11 @@ def attend_head(q, k, v, scale, causal, q_pos=None, return_weights=False,
 
     q: [M, d] query rows; k, v: [N, d] keys and values of the head.
     scale: the softmax scale (used as given, widened to float64).
-    causal: if true, query row r sees keys 0..q_pos[r] only.
-    q_pos: position of each query row on the key axis (default 0..M-1, i.e. the
-      rows are the head's first M queries). Lets a test check a sample of rows.
+    causal: if true, query row r sees keys 0..q_pos[r] only (none if q_pos[r]
+      is negative: that row gets o = 0, lse = -inf).
+    q_pos: position of each query row on the key axis (default r + N - M, the
+      M queries aligned with the end of the N keys; r for M == N). Lets a
+      test check a sample of rows.
     return_weights: also return the normalised weights [M, N] (debug aid).
     """
     q = np.asarray(q, dtype=np.float64)
@@ -56,10 +61,8 @@ def attend_head(q, k, v, scale, causal, q_pos=None, return_weights=False,
     if k.shape != (n_keys, d) or v.shape[0] != n_keys:
         raise ValueError("q, k, v shapes do not agree")
     if q_pos is None:
-        q_pos = np.arange(m_rows)
+        q_pos = np.arange(m_rows) + (n_keys - m_rows)
     q_pos = np.asarray(q_pos, dtype=np.int64)
-    if causal and m_rows and (q_pos.min() < 0 or q_pos.max() >= n_keys):
-        raise ValueError("causal query positions must lie on the key axis")
 
     o = np.empty((m_rows, v.shape[1]), dtype=np.float64)
     lse = np.empty(m_rows, dtype=np.float64)
@@ -73,11 +76,15 @@ def attend_head(q, k, v, scale, causal, q_pos=None, return_weights=False,
             hidden = key_idx[None, :] > q_pos[r0:r1, None]
             s[hidden] = -np.inf
         # safe softmax: subtract the row maximum, exponentiate, normalise
-        m = s.max(axis=1, keepdims=True)
+        m = s.max(axis=1, keepdims=True) if n_keys else np.full((r1 - r0, 1), -np.inf)
+        empty = ~np.isfinite(m[:, 0]) & (m[:, 0] < 0)  # no visible key
+        m[empty] = 0.0
         w = np.exp(s - m)  # masked entries: exp(-inf) == 0 exactly
         l = w.sum(axis=1, keepdims=True)
+        l[empty] = 1.0  # empty sum: o = 0 below, lse = -inf
         o[r0:r1] = (w @ v) / l
         lse[r0:r1] = m[:, 0] + np.log(l[:, 0])
+        lse[r0:r1][empty] = -np.inf
         if return_weights:
             weights[r0:r1] = w / l
     if return_weights:
@@ -86,17 +93,19 @@ def attend_head(q, k, v, scale, causal, q_pos=None, return_weights=False,
 
 
 def attention_ref(q, k, v, scale, causal):
-    """Attention over a [B, H, N, d] batch: returns (o [B,H,N,d], lse [B,H,N]).
+    """Attention over a batch: q [B, H, M, d], k and v [B, H, N, d]; returns
+    (o [B,H,M,d], lse [B,H,M]). M == N is the usual self-attention shape.
 
     Every (b, h) pair is an independent head; each is handed to attend_head.
     """
     q = np.asarray(q)
     k = np.asarray(k)
     v = np.asarray(v)
-    if q.ndim != 4 or k.shape != q.shape or v.shape[:3] != q.shape[:3]:
-        raise ValueError("expected q, k, v of shape [B, H, N, d]")
+    if (q.ndim != 4 or k.ndim != 4 or k.shape[:2] != q.shape[:2] or k.shape[3] != q.shape[3]
+            or v.shape[:3] != k.shape[:3]):
+        raise ValueError("expected q [B, H, M, d] and k, v [B, H, N, d]")
     b_n, h_n, n, _ = q.shape
-    o = np.empty(v.shape, dtype=np.float64)
+    o = np.empty((b_n, h_n, n, v.shape[3]), dtype=np.float64)
     lse = np.empty((b_n, h_n, n), dtype=np.float64)
     for b in range(b_n):
         for h in range(h_n):

@@ -39,7 +39,8 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["attn_fwd", "attn_fwd_launch_shape", "attn_strerror"]
+    assert declared_functions() == ["attn_fwd", "attn_fwd_cross", "attn_fwd_launch_shape",
+                                    "attn_strerror"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -169,3 +170,38 @@ def test_binding_rejects_bad_tensors():
         mi.attn_fwd(q.float(), q, q)
     with pytest.raises(TypeError):
         mi.attn_fwd([1], q, q)
+
+
+# ------------------------------------------------------ attn_fwd_cross --
+
+def cross(lib, q=Q, k=K, v=V, o=O, lse=L, B=2, H=3, Nq=100, Nk=70, d=128, scale=0.125,
+          causal=0):
+    return lib.attn_fwd_cross(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, None)
+
+
+@pytest.mark.parametrize("Nq,Nk", [(-1, 4), (4, -1)])
+def test_cross_negative_lengths(lib, Nq, Nk):
+    assert cross(lib, Nq=Nq, Nk=Nk) == ERR_SHAPE
+
+
+def test_cross_null_and_empty(lib):
+    assert cross(lib, q=None) == ERR_NULL
+    assert cross(lib, k=None) == ERR_NULL
+    # no keys: k and v may be NULL (every row is empty); still validated, not
+    # launched here because o aliases q
+    assert cross(lib, k=None, v=None, Nk=0, o=Q) == ERR_ALIAS
+    # no queries: nothing to do
+    assert cross(lib, q=None, k=None, v=None, o=None, lse=None, Nq=0) == OK
+
+
+def test_cross_aliasing_uses_each_tensors_size(lib):
+    # o (Nq rows) placed right after a k of Nk rows: no overlap -> would launch;
+    # placed inside k -> rejected.
+    kbytes = 2 * 3 * 70 * 128 * 2
+    assert cross(lib, o=K + kbytes - 256) == ERR_ALIAS
+    assert cross(lib, lse=V + 4) == ERR_ALIAS
+
+
+def test_cross_headdim_and_scale(lib):
+    assert cross(lib, d=96) == ERR_HEADDIM
+    assert cross(lib, scale=float("nan")) == ERR_SCALE

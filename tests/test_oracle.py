@@ -28,6 +28,8 @@ GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_examples.txt")
 
 def _entry(tok):
     tok = tok.strip()
+    if tok == "-inf":
+        return -math.inf
     if tok.startswith("ln(") and tok.endswith(")"):
         return math.log(float(Fraction(tok[3:-1])))
     return float(Fraction(tok))
@@ -75,19 +77,26 @@ def _rand(shape, seed, std=1.0):
 def pin_golden(attend):
     for c in GOLDEN_CASES:
         o, lse = attend(c["Q"], c["K"], c["V"], c["scale"], c["causal"])
+        finite = np.isfinite(c["lse"])
         if not (np.allclose(o, c["O"], rtol=0, atol=1e-13)
-                and np.allclose(lse, c["lse"], rtol=0, atol=1e-13)):
+                and np.array_equal(np.isfinite(lse), finite)
+                and np.allclose(lse[finite], c["lse"][finite], rtol=0, atol=1e-13)
+                and np.all(lse[~finite] == -np.inf)):
             return False
     return True
 
 
 def pin_rows_are_distributions(attend):
+    """Weights are distributions; causal weights vanish above the diagonal
+    that ends both axes together (19 queries, 23 keys: query i at key i+4)."""
     q, k, v = _rand((19, 8), 1), _rand((23, 8), 2), _rand((23, 5), 3)
     for causal in (False, True):
         _, _, w = attend(q, k, v, 0.7, causal, return_weights=True)
         if np.abs(w.sum(axis=1) - 1).max() > 1e-14 or w.min() < 0:
             return False
-        if causal and np.any(np.triu(w, 1) != 0):
+        if causal and np.any(np.triu(w, 1 + 23 - 19) != 0):
+            return False
+        if causal and np.any(np.diagonal(w, 23 - 19) == 0):
             return False
     return True
 
@@ -283,7 +292,8 @@ def _mutant(kind):
         k = np.asarray(k, dtype=np.float64)
         v = np.asarray(v, dtype=np.float64)
         n_q, n_k = q.shape[0], k.shape[0]
-        pos = np.arange(n_q) if q_pos is None else np.asarray(q_pos)
+        offset = 0 if kind == "top_left_alignment" else n_k - n_q
+        pos = np.arange(n_q) + offset if q_pos is None else np.asarray(q_pos)
         if kind == "transposed_scores":
             if n_q != n_k:
                 s = scale * (q @ k.T)
@@ -301,6 +311,9 @@ def _mutant(kind):
             hidden = {"causal_flipped": j < i, "causal_off_by_one": j >= i}.get(kind, j > i)
             s = np.where(hidden, -np.inf, s)
         m = s.max(axis=1, keepdims=True)
+        empty = np.isneginf(m[:, 0])
+        if kind != "empty_rows_nan":
+            m[empty] = 0.0
         if kind == "no_max_subtraction":
             w = np.exp(s)
             m = np.zeros_like(m)
@@ -310,6 +323,8 @@ def _mutant(kind):
             w = np.exp(s - m)
         axis = 0 if kind == "softmax_over_queries" else 1
         l = w.sum(axis=axis, keepdims=True)
+        if kind != "empty_rows_nan" and axis == 1:
+            l[empty] = 1.0
         o = w @ v if kind == "not_normalised" else (w / l) @ v
         if kind == "values_rows_reversed":
             o = (w / l) @ v[::-1]
@@ -322,6 +337,8 @@ def _mutant(kind):
             lse = m[:, 0] / scale + np.log(lse_l) if scale != 0 else m[:, 0] + np.log(lse_l)
         else:
             lse = m[:, 0] + np.log(lse_l)
+        if kind != "empty_rows_nan" and axis == 1:
+            lse = np.where(empty, -np.inf, lse)
         if return_weights:
             return o, lse, w / l
         return o, lse
@@ -331,7 +348,7 @@ def _mutant(kind):
 MUTANTS = ["transposed_scores", "scale_dropped", "scale_squared", "causal_flipped",
            "causal_off_by_one", "no_max_subtraction", "softmax_over_queries",
            "not_normalised", "values_rows_reversed", "lse_base2", "lse_without_max",
-           "lse_of_unscaled"]
+           "lse_of_unscaled", "top_left_alignment", "empty_rows_nan"]
 
 
 @pytest.mark.parametrize("kind", MUTANTS)

@@ -228,3 +228,82 @@ def test_rejections_leave_outputs_untouched():
         mi.attn_fwd(q, q, q, scale=float("nan"), out=out, lse=lse)
     torch.cuda.synchronize()
     assert bool((out == 7).all()) and bool((lse == 7).all())
+
+
+# ---------------------------------------------- queries and keys of two lengths --
+
+def run_cross(q, k, v, scale, causal):
+    dev = torch.device("cuda:0")
+    o, lse = mi.attn_fwd_cross(q.to(dev), k.to(dev), v.to(dev), scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy(), lse.cpu().numpy()
+
+
+def check_with_empty_rows(o, lse, o_ref, lse_ref, what):
+    """Like check(), but rows that see no key must be exactly o = 0, lse = -inf."""
+    empty = np.isneginf(lse_ref)
+    assert np.array_equal(np.isneginf(lse), empty), f"{what}: empty rows differ"
+    assert np.all(o[empty] == 0.0), f"{what}: empty rows must be zero"
+    check(o[~empty], lse[~empty], o_ref[~empty], lse_ref[~empty], what)
+
+
+CROSS = [(1, 1), (3, 2), (2, 3), (100, 37), (37, 100), (129, 1000), (1000, 129),
+         (256, 64), (64, 256), (200, 1)]
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("Nq,Nk", CROSS)
+def test_cross_lengths(Nq, Nk, d, causal):
+    """Nq queries against Nk keys, causal aligned at the ends of both axes."""
+    announce(f"cross Nq={Nq} Nk={Nk} d={d} causal={causal}")
+    qi = make_inputs(WORKLOADS[1], B=2, H=2, N=Nq, d=d, seed=2000 + Nq)
+    ki = make_inputs(WORKLOADS[1], B=2, H=2, N=Nk, d=d, seed=3000 + Nk)
+    o, lse = run_cross(qi["q"], ki["k"], ki["v"], qi["scale"], causal)
+    o_ref, lse_ref = attention_ref(as64(qi["q"]), as64(ki["k"]), as64(ki["v"]),
+                                   qi["scale"], causal)
+    check_with_empty_rows(o, lse, o_ref, lse_ref, f"cross {Nq}x{Nk}")
+
+
+def test_cross_without_keys():
+    announce("cross Nk=0")
+    dev = torch.device("cuda:0")
+    q = torch.randn(1, 2, 70, 64).to(torch.bfloat16).to(dev)
+    k = torch.zeros(1, 2, 0, 64, dtype=torch.bfloat16, device=dev)
+    o, lse = mi.attn_fwd_cross(q, k, k, causal=False)
+    torch.cuda.synchronize()
+    assert bool((o == 0).all()) and bool(torch.isneginf(lse).all())
+
+
+def test_cross_equals_self_attention_when_lengths_match():
+    announce("cross == self")
+    inp = make_inputs(WORKLOADS[3], B=1, H=2, N=300, d=128, seed=14)
+    dev = torch.device("cuda:0")
+    q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+    for causal in (False, True):
+        o1, l1 = mi.attn_fwd(q, k, v, scale=inp["scale"], causal=causal)
+        o2, l2 = mi.attn_fwd_cross(q, k, v, scale=inp["scale"], causal=causal)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_hand_examples_on_gpu():
+    """The hand-derived examples, zero-padded to d=64 (scores unchanged, the
+    padded output columns are 0), against the oracle on the same bf16 values."""
+    from tests.test_oracle import GOLDEN_CASES
+    for c in GOLDEN_CASES:
+        announce(f"golden {c['name']}")
+        def pad(a):
+            t = torch.zeros(1, 1, a.shape[0], 64, dtype=torch.float64)
+            t[0, 0, :, :a.shape[1]] = torch.from_numpy(a)
+            return t.to(torch.bfloat16)
+        q, k, v = pad(c["Q"]), pad(c["K"]), pad(c["V"])
+        scale = float(np.float32(c["scale"]))
+        o, lse = run_cross(q, k, v, scale, c["causal"])
+        o_ref, lse_ref = attention_ref(as64(q), as64(k), as64(v), scale, c["causal"])
+        check_with_empty_rows(o, lse, o_ref, lse_ref, c["name"])
+        # and the exact values, within the bf16 rounding of the inputs
+        nd = c["O"].shape[1]
+        fin = np.isfinite(c["lse"])
+        assert np.allclose(o[0, 0, :, :nd], c["O"], atol=0.05)
+        assert np.allclose(lse[0, 0][fin], c["lse"][fin], atol=0.05)

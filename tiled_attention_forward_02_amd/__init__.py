@@ -13,8 +13,8 @@ import ctypes
 import math
 import os
 
-__all__ = ["attn_fwd", "attn_strerror", "attn_fwd_launch_shape", "lib_path",
-           "load_library", "AttnError"]
+__all__ = ["attn_fwd", "attn_fwd_cross", "attn_strerror", "attn_fwd_launch_shape",
+           "lib_path", "load_library", "AttnError"]
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmi_attn.so")
 _lib = None
@@ -45,6 +45,8 @@ def load_library():
     vp, i32, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, i32, vp]
     lib.attn_fwd.restype = i32
+    lib.attn_fwd_cross.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp]
+    lib.attn_fwd_cross.restype = i32
     lib.attn_strerror.argtypes = [i32]
     lib.attn_strerror.restype = ctypes.c_char_p
     ip = ctypes.POINTER(i32)
@@ -70,6 +72,58 @@ def attn_fwd_launch_shape(B, H, N, d, causal=False):
                     (x.value for x in out)))
 
 
+def _check_inputs(q, k, v):
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if t.dtype != torch.bfloat16:
+            raise TypeError(f"{name} must be bfloat16, got {t.dtype}")
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be on a HIP device, got {t.device}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous [B, H, N, d]")
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
+        raise ValueError(f"q, k, v must be [B, H, N, d] with k and v alike, got "
+                         f"{tuple(q.shape)}, {tuple(k.shape)}, {tuple(v.shape)}")
+    if k.shape[:2] != q.shape[:2] or k.shape[3] != q.shape[3]:
+        raise ValueError(f"q and k must share B, H and d, got {tuple(q.shape)}, {tuple(k.shape)}")
+    if k.device != q.device or v.device != q.device:
+        raise ValueError("q, k, v must be on one device")
+
+
+def _outputs(q, out, lse):
+    import torch
+
+    B, H, Nq, _ = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    elif (out.shape != q.shape or out.dtype != torch.bfloat16
+          or out.device != q.device or not out.is_contiguous()):
+        raise ValueError("out must be a contiguous bf16 tensor shaped like q")
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    elif (tuple(lse.shape) != (B, H, Nq) or lse.dtype != torch.float32
+          or lse.device != q.device or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous float32 tensor [B, H, Nq]")
+    return out, lse
+
+
+def _stream_handle(q, stream):
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+
+
+def _default_scale(d):
+    import torch
+
+    return float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32))
+
+
 def attn_fwd(q, k, v, scale=None, causal=False, out=None, lse=None, stream=None):
     """O, lse = attention forward of bf16 tensors q, k, v [B, H, N, d].
 
@@ -81,40 +135,43 @@ def attn_fwd(q, k, v, scale=None, causal=False, out=None, lse=None, stream=None)
     import torch
 
     lib = load_library()
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        if not isinstance(t, torch.Tensor):
-            raise TypeError(f"{name} must be a torch.Tensor")
-        if t.dtype != torch.bfloat16:
-            raise TypeError(f"{name} must be bfloat16, got {t.dtype}")
-        if t.device.type != "cuda":
-            raise ValueError(f"{name} must be on a HIP device, got {t.device}")
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous [B, H, N, d]")
-    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
+    _check_inputs(q, k, v)
+    if k.shape != q.shape:
         raise ValueError(f"q, k, v must share one [B, H, N, d] shape, got "
                          f"{tuple(q.shape)}, {tuple(k.shape)}, {tuple(v.shape)}")
-    if k.device != q.device or v.device != q.device:
-        raise ValueError("q, k, v must be on one device")
     B, H, N, d = q.shape
-    if scale is None:
-        scale = float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32))
-    if out is None:
-        out = torch.empty_like(q)
-    elif (out.shape != q.shape or out.dtype != torch.bfloat16
-          or out.device != q.device or not out.is_contiguous()):
-        raise ValueError("out must be a contiguous bf16 tensor shaped like q")
-    if lse is None:
-        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    elif (tuple(lse.shape) != (B, H, N) or lse.dtype != torch.float32
-          or lse.device != q.device or not lse.is_contiguous()):
-        raise ValueError("lse must be a contiguous float32 tensor [B, H, N]")
+    scale = _default_scale(d) if scale is None else scale
+    out, lse = _outputs(q, out, lse)
     with torch.cuda.device(q.device):
-        if stream is None:
-            stream = torch.cuda.current_stream(q.device)
-        handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
         rc = lib.attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                           lse.data_ptr(), B, H, N, d, float(scale), int(bool(causal)),
-                          handle)
+                          _stream_handle(q, stream))
+    if rc:
+        raise AttnError(rc, attn_strerror(rc))
+    return out, lse
+
+
+def attn_fwd_cross(q, k, v, scale=None, causal=False, out=None, lse=None, stream=None):
+    """O, lse = attention forward of q [B, H, Nq, d] against k, v [B, H, Nk, d].
+
+    causal aligns the query and key axes at their ends (query i sees keys
+    j <= i + Nk - Nq); a query that sees no key gets o = 0 and lse = -inf.
+    Other arguments as for attn_fwd.
+    """
+    import torch
+
+    lib = load_library()
+    _check_inputs(q, k, v)
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    scale = _default_scale(d) if scale is None else scale
+    out, lse = _outputs(q, out, lse)
+    kp = k.data_ptr() if Nk else 0
+    vp = v.data_ptr() if Nk else 0
+    with torch.cuda.device(q.device):
+        rc = lib.attn_fwd_cross(q.data_ptr(), kp, vp, out.data_ptr(), lse.data_ptr(),
+                                B, H, Nq, Nk, d, float(scale), int(bool(causal)),
+                                _stream_handle(q, stream))
     if rc:
         raise AttnError(rc, attn_strerror(rc))
     return out, lse

@@ -47,6 +47,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <float.h>
 #include <string.h>
 
 #include <type_traits>
@@ -170,7 +171,7 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, kBlockN<D> == 32 ? 3 : 2) void attn_fwd_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     const __bf16* __restrict__ V, __bf16* __restrict__ O,
-    float* __restrict__ LSE, int BH, int N, int nq, float c) {
+    float* __restrict__ LSE, int BH, int Nq, int Nk, int nq, float c) {
   using T = Tile<D, kBlockN<D>>;
   constexpr int BN = T::BN, KS = T::KS, CPR = T::CPR, KPT = T::KPT, NKB = T::NKB;
   __shared__ __attribute__((aligned(16))) __bf16 smem[T::LDS_ELEMS];
@@ -184,11 +185,16 @@ __global__ __launch_bounds__(kThreads, kBlockN<D> == 32 ? 3 : 2) void attn_fwd_k
   const int qw = q0 + 32 * wave;  // first query row of this wave
   const int qi = qw + col;        // this lane's query row
 
-  const size_t head = (size_t)bh * (size_t)N * D;
-  const uint32_t head_bytes = (uint32_t)N * D * 2;
-  const rsrc_t rq = make_rsrc(Q + head, head_bytes);
-  const rsrc_t rk = make_rsrc(K + head, head_bytes);
-  const rsrc_t rv = make_rsrc(V + head, head_bytes);
+  // Query rows live on [0, Nq), keys on [0, Nk); query i sits at key position
+  // i + off (the two axes aligned at their ends; off = 0 when Nq == Nk).
+  const int off = Nk - Nq;
+  const size_t qhead = (size_t)bh * (size_t)Nq * D;
+  const size_t khead = (size_t)bh * (size_t)Nk * D;
+  const uint32_t q_bytes = (uint32_t)Nq * D * 2;
+  const uint32_t k_bytes = (uint32_t)Nk * D * 2;
+  const rsrc_t rq = make_rsrc(Q + qhead, q_bytes);
+  const rsrc_t rk = make_rsrc(K + khead, k_bytes);
+  const rsrc_t rv = make_rsrc(V + khead, k_bytes);
 
   // Q^T fragments (B operand): lane holds Q[qi][16s + 8h .. +7]; zero past N.
   u32x4 qraw[D / 16];
@@ -212,9 +218,10 @@ __global__ __launch_bounds__(kThreads, kBlockN<D> == 32 ? 3 : 2) void attn_fwd_k
   for (int s = 0; s < D / 16; ++s) qf[s] = __builtin_bit_cast(bf16x8, qraw[s]);
 
   // Keys this workgroup / this wave can see.
-  const int kv_end = CAUSAL ? min(N, q0 + kBlockM) : N;
-  const int nt = (kv_end + BN - 1) / BN;
-  const int wave_kv_end = CAUSAL ? min(N, qw + 32) : N;
+  // Keys this workgroup / this wave can see (none for rows before -off).
+  const int kv_end = CAUSAL ? min(Nk, q0 + kBlockM + off) : Nk;
+  const int nt = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
+  const int wave_kv_end = CAUSAL ? min(Nk, qw + 32 + off) : Nk;
 
   // Staging. K: thread owns rows kr_k .. +KPT-1, 16-byte chunk dc_k, with the
   // chunk fastest across lanes (whole rows per 16 lanes: coalesced loads,
@@ -240,12 +247,21 @@ __global__ __launch_bounds__(kThreads, kBlockN<D> == 32 ? 3 : 2) void attn_fwd_k
   // Per-lane LDS byte offsets that do not change with the tile.
   const uint32_t k_wr = (uint32_t)(kr_k * KS + 8 * dc_k) * 2;
   const int vpos = 16 * (kr_v >> 4) + slice_pos(kr_v & 15);
+  // With 64-byte V^T rows (32-key tiles), odd 16-lane groups write the
+  // chunk's columns in the order e ^ 1, so the two groups that share an LDS
+  // cycle write rows of opposite parity instead of the same banks (measured:
+  // a third fewer bank-conflict cycles).
+  const int vflip = BN == 32 ? (tid >> 4) & 1 : 0;
   uint32_t v_wr[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const int d = 8 * dc_v + e;
+    const int d = 8 * dc_v + (e ^ vflip);
     v_wr[e] = (uint32_t)(T::K_ELEMS + d * BN + ((vpos >> 3) ^ vt_swz<BN>(d)) * 8 + (vpos & 7)) * 2;
   }
+  // v_perm selectors for the bf16 at an even (0x05040100) or odd (0x07060302)
+  // column of a 32-bit word, swapped for the flipped lane groups.
+  const uint32_t sel_even = vflip ? 0x07060302u : 0x05040100u;
+  const uint32_t sel_odd = vflip ? 0x05040100u : 0x07060302u;
   const uint32_t k_rd = (uint32_t)(col * KS + 8 * half) * 2;
   uint32_t v_rd[BN / 16];  // V^T read of 16-key slice g, rows 32*db + col (db: immediate)
 #pragma unroll
@@ -262,9 +278,8 @@ __global__ __launch_bounds__(kThreads, kBlockN<D> == 32 ? 3 : 2) void attn_fwd_k
       *reinterpret_cast<u32x4*>(lds + base + k_wr + i * KS * 2) = kst[i];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const int w = e >> 1;
-      // bytes of the bf16 at even (0x05040100) or odd (0x07060302) column e
-      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+      const int w = e >> 1;  // the same word for column e and e ^ 1
+      const uint32_t sel = (e & 1) ? sel_odd : sel_even;
       const uint32_t lo = __builtin_amdgcn_perm(vst[1][w], vst[0][w], sel);
       if constexpr (KPT == 4) {
         const uint32_t hi = __builtin_amdgcn_perm(vst[3][w], vst[2][w], sel);
@@ -278,7 +293,9 @@ __global__ __launch_bounds__(kThreads, kBlockN<D> == 32 ? 3 : 2) void attn_fwd_k
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
-  float m_run = -INFINITY;  // reference maximum of O and l, log2 units
+  // Reference maximum of O and l (log2 units). It starts at -FLT_MAX, not
+  // -inf, so that a row with no visible key keeps l = 0 without NaN.
+  float m_run = -FLT_MAX;
   float l_run = 0.f;        // this lane's share of the row sum
 
   // One tile: S^T, mask, running max, P, O^T += V^T P^T; then stage the next.
@@ -304,13 +321,13 @@ __global__ __launch_bounds__(kThreads, kBlockN<D> == 32 ? 3 : 2) void attn_fwd_k
       }
 
       // Keys past the end and (causal) keys after the query get -inf.
-      if ((k0 + BN > N) || (CAUSAL && k0 + BN - 1 > qw)) {
+      if ((k0 + BN > Nk) || (CAUSAL && k0 + BN - 1 > qw + off)) {
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int key = k0 + 32 * kb + 8 * (i >> 2) + 4 * half + (i & 3);
-            if (key >= N || (CAUSAL && key > qi)) sacc[kb][i] = -INFINITY;
+            if (key >= Nk || (CAUSAL && key > qi + off)) sacc[kb][i] = -INFINITY;
           }
       }
 
@@ -395,8 +412,9 @@ __global__ __launch_bounds__(kThreads, kBlockN<D> == 32 ? 3 : 2) void attn_fwd_k
   // Epilogue: O = acc / l (bf16), lse = (m + log2 l) * ln 2. Rows past N are
   // dropped by the buffer range check.
   const float total = swap_halves_add(l_run);
-  const float inv = 1.0f / total;
-  const rsrc_t ro = make_rsrc(O + head, head_bytes);
+  // A row that saw no key (l = 0) gets O = 0 and lse = -inf.
+  const float inv = total > 0.f ? 1.0f / total : 0.f;
+  const rsrc_t ro = make_rsrc(O + qhead, q_bytes);
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
@@ -410,8 +428,8 @@ __global__ __launch_bounds__(kThreads, kBlockN<D> == 32 ? 3 : 2) void attn_fwd_k
     }
   }
   if (half == 0) {
-    const rsrc_t rl = make_rsrc(LSE + (size_t)bh * N, (uint32_t)N * 4);
-    const float lse = (m_run + log2f(total)) * kLn2;
+    const rsrc_t rl = make_rsrc(LSE + (size_t)bh * Nq, (uint32_t)Nq * 4);
+    const float lse = total > 0.f ? (m_run + log2f(total)) * kLn2 : -INFINITY;
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lse), rl, qi * 4, 0, 0);
   }
 }
@@ -422,13 +440,15 @@ struct Shape {
   int grid, block, lds, block_m, block_n, nq;
 };
 
-int check_sizes(int B, int H, int N, int d, Shape* sh) {
-  if (B < 0 || H < 0 || N < 0) return ATTN_ERR_SHAPE;
+// Sizes shared by every entry point; Nk only bounds the key tensors.
+int check_sizes(int B, int H, int Nq, int Nk, int d, Shape* sh) {
+  if (B < 0 || H < 0 || Nq < 0 || Nk < 0) return ATTN_ERR_SHAPE;
   if (d != 64 && d != 128) return ATTN_ERR_HEADDIM;
-  // One head's tensor is addressed with 32-bit byte offsets.
-  if ((int64_t)N * d * 2 + (int64_t)kBlockM * d * 2 > INT32_MAX) return ATTN_ERR_SHAPE;
+  // One head's tensors are addressed with 32-bit byte offsets.
+  if ((int64_t)Nq * d * 2 + (int64_t)kBlockM * d * 2 > INT32_MAX) return ATTN_ERR_SHAPE;
+  if ((int64_t)Nk * d * 2 + (int64_t)kBlockN<64> * 128 * 2 > INT32_MAX) return ATTN_ERR_SHAPE;
   if ((int64_t)B * H > INT32_MAX) return ATTN_ERR_SHAPE;
-  const int64_t nq = ((int64_t)N + kBlockM - 1) / kBlockM;
+  const int64_t nq = ((int64_t)Nq + kBlockM - 1) / kBlockM;
   const int64_t grid = (int64_t)B * H * nq;
   if (grid > INT32_MAX) return ATTN_ERR_SHAPE;
   sh->grid = (int)grid;
@@ -441,44 +461,44 @@ int check_sizes(int B, int H, int N, int d, Shape* sh) {
 }
 
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || !na || !nb) return false;
   const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
   return x < y + nb && y < x + na;
 }
 
 template <int D, bool CAUSAL>
 hipError_t launch(const Shape& sh, const void* q, const void* k, const void* v, void* o,
-                  float* lse, int BH, int N, float c, hipStream_t stream) {
+                  float* lse, int BH, int Nq, int Nk, float c, hipStream_t stream) {
   const __bf16* qp = static_cast<const __bf16*>(q);
   const __bf16* kp = static_cast<const __bf16*>(k);
   const __bf16* vp = static_cast<const __bf16*>(v);
   __bf16* op = static_cast<__bf16*>(o);
   int nq = sh.nq;
-  void* args[] = {&qp, &kp, &vp, &op, &lse, &BH, &N, &nq, &c};
+  void* args[] = {&qp, &kp, &vp, &op, &lse, &BH, &Nq, &Nk, &nq, &c};
   return hipLaunchKernel(reinterpret_cast<const void*>(&attn_fwd_kernel<D, CAUSAL>),
                          dim3(sh.grid), dim3(sh.block), args, 0, stream);
 }
 
-}  // namespace
-
-extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
-                        int B, int H, int N, int d, float scale, int causal,
-                        void* stream) {
+// Validation and launch behind attn_fwd and attn_fwd_cross.
+int run(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+        int Nq, int Nk, int d, float scale, int causal, void* stream) {
   Shape sh;
-  const int rc = check_sizes(B, H, N, d, &sh);
+  const int rc = check_sizes(B, H, Nq, Nk, d, &sh);
   if (rc != ATTN_OK) return rc;
   uint32_t sbits;
   memcpy(&sbits, &scale, 4);
   if ((sbits & 0x7f800000u) == 0x7f800000u) return ATTN_ERR_SCALE;  // NaN or +-inf
-  if (sh.grid == 0) return ATTN_OK;  // B*H*N == 0: nothing to compute
-  if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL;
+  if (sh.grid == 0) return ATTN_OK;  // B*H*Nq == 0: nothing to compute
+  if (!q || !o || !lse || (Nk > 0 && (!k || !v))) return ATTN_ERR_NULL;
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15) return ATTN_ERR_ALIGN;
   if ((uintptr_t)lse & 3) return ATTN_ERR_ALIGN;
-  const size_t tbytes = (size_t)B * H * N * d * 2;
-  const size_t lbytes = (size_t)B * H * N * 4;
-  if (overlaps(o, tbytes, q, tbytes) || overlaps(o, tbytes, k, tbytes) ||
-      overlaps(o, tbytes, v, tbytes) || overlaps(lse, lbytes, q, tbytes) ||
-      overlaps(lse, lbytes, k, tbytes) || overlaps(lse, lbytes, v, tbytes) ||
-      overlaps(lse, lbytes, o, tbytes))
+  const size_t qbytes = (size_t)B * H * Nq * d * 2;
+  const size_t kbytes = (size_t)B * H * Nk * d * 2;
+  const size_t lbytes = (size_t)B * H * Nq * 4;
+  if (overlaps(o, qbytes, q, qbytes) || overlaps(o, qbytes, k, kbytes) ||
+      overlaps(o, qbytes, v, kbytes) || overlaps(lse, lbytes, q, qbytes) ||
+      overlaps(lse, lbytes, k, kbytes) || overlaps(lse, lbytes, v, kbytes) ||
+      overlaps(lse, lbytes, o, qbytes))
     return ATTN_ERR_ALIAS;
 
   const float c = scale * kLog2e;
@@ -486,20 +506,34 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, fl
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t err;
   if (d == 64) {
-    err = causal ? launch<64, true>(sh, q, k, v, o, lse, BH, N, c, st)
-                 : launch<64, false>(sh, q, k, v, o, lse, BH, N, c, st);
+    err = causal ? launch<64, true>(sh, q, k, v, o, lse, BH, Nq, Nk, c, st)
+                 : launch<64, false>(sh, q, k, v, o, lse, BH, Nq, Nk, c, st);
   } else {
-    err = causal ? launch<128, true>(sh, q, k, v, o, lse, BH, N, c, st)
-                 : launch<128, false>(sh, q, k, v, o, lse, BH, N, c, st);
+    err = causal ? launch<128, true>(sh, q, k, v, o, lse, BH, Nq, Nk, c, st)
+                 : launch<128, false>(sh, q, k, v, o, lse, BH, Nq, Nk, c, st);
   }
   return err == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                        int B, int H, int N, int d, float scale, int causal,
+                        void* stream) {
+  return run(q, k, v, o, lse, B, H, N, N, d, scale, causal, stream);
+}
+
+extern "C" int attn_fwd_cross(const void* q, const void* k, const void* v, void* o,
+                              float* lse, int B, int H, int Nq, int Nk, int d, float scale,
+                              int causal, void* stream) {
+  return run(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, stream);
 }
 
 extern "C" const char* attn_strerror(int status) {
   switch (status) {
     case ATTN_OK: return "success";
     case ATTN_ERR_NULL: return "null pointer argument";
-    case ATTN_ERR_SHAPE: return "invalid shape: B, H, N must be >= 0 and the sizes must fit";
+    case ATTN_ERR_SHAPE: return "invalid shape: sizes must be >= 0 and fit 32-bit head offsets";
     case ATTN_ERR_HEADDIM: return "unsupported head dimension: d must be 64 or 128";
     case ATTN_ERR_ALIGN: return "misaligned pointer: q, k, v, o need 16 bytes, lse 4 bytes";
     case ATTN_ERR_ALIAS: return "output buffer overlaps an input or the other output";
@@ -515,7 +549,7 @@ extern "C" int attn_fwd_launch_shape(int B, int H, int N, int d, int causal, int
   (void)causal;
   if (!grid || !block || !lds_bytes || !block_m || !block_n) return ATTN_ERR_NULL;
   Shape sh;
-  const int rc = check_sizes(B, H, N, d, &sh);
+  const int rc = check_sizes(B, H, N, N, d, &sh);
   if (rc != ATTN_OK) return rc;
   *grid = sh.grid;
   *block = sh.block;
