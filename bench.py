@@ -1,18 +1,22 @@
 """Benchmark of the fused attention forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--head-dim D] [--dtype bf16|f16]
                     [--no-cpu-baseline] [--copy-calibration MIB]
 
 A step is one attn_fwd call over the whole workload (every query row of every
 (batch, head)) with inputs already resident in HBM. The default workload is
 the non-causal d=128, N=4096 one (B=16, H=16) that the throughput target is
-quoted on. Prints ONE JSON line on stdout; diagnostics go to stderr.
+quoted on. --head-dim and --dtype keep the workload's B, H, N and causality
+and change the head dimension (32, 64, 128, 256) or the element type (float16
+goes through attn_fwd_ex); the workload name then carries the change. Prints
+ONE JSON line on stdout; diagnostics go to stderr.
 
 FLOP per step follow the metric: 4*B*H*N^2*d, halved when causal.
 roofline.achieved = FLOP per launch / average launch duration, the duration
 taken with HIP events on the stream the kernel is launched on. Peak is the
-MI355X dense bf16 MFMA figure, 2516.6 TFLOP/s (256 CU x 4096 FLOP/clk x 2.4
-GHz). roofline.traffic (HBM bytes per launch) comes from the rocprofv3
+MI355X dense bf16 (and fp16) MFMA figure, 2516.6 TFLOP/s (256 CU x 4096
+FLOP/clk x 2.4 GHz). roofline.traffic (HBM bytes per launch) comes from the rocprofv3
 FETCH_SIZE / WRITE_SIZE summary committed under profiles/, and is null when
 that summary was taken on a different kernel source.
 
@@ -27,7 +31,9 @@ import argparse
 import hashlib
 import json
 import math
+import dataclasses
 import os
+import re
 import sys
 import time
 
@@ -142,6 +148,8 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--head-dim", type=int, default=0, choices=[0, 32, 64, 128, 256])
+    ap.add_argument("--dtype", default="bf16", choices=["bf16", "f16"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
@@ -168,17 +176,26 @@ def main():
         return
 
     w = workload(args.workload)
+    if args.head_dim and args.head_dim != w.d:
+        w = dataclasses.replace(w, d=args.head_dim,
+                                name=re.sub(r"d\d+$", f"d{args.head_dim}", w.name))
+    elem = torch.bfloat16
+    if args.dtype == "f16":
+        w = dataclasses.replace(w, name=w.name + "_f16")
+        elem = torch.float16
     dev = torch.device("cuda:0")
-    log(f"workload {w.name}: B={w.B} H={w.H} N={w.N} d={w.d} causal={w.causal}")
-    inp = make_inputs(w)
+    log(f"workload {w.name}: B={w.B} H={w.H} N={w.N} d={w.d} causal={w.causal} {args.dtype}")
+    inp = make_inputs(w, dtype=elem)
     q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
     shape = mi.attn_fwd_launch_shape(w.B, w.H, w.N, w.d, w.causal)
     log(f"launch: {shape}")
 
+    fwd = mi.attn_fwd if args.dtype == "bf16" else mi.attn_fwd_ex
+
     def step():
-        mi.attn_fwd(q, k, v, scale=inp["scale"], causal=w.causal, out=o, lse=lse)
+        fwd(q, k, v, scale=inp["scale"], causal=w.causal, out=o, lse=lse)
 
     step()
     torch.cuda.synchronize()
@@ -228,7 +245,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": args.dtype,
         "data": "synthetic",
         "config": w.as_dict(),
         "roofline": {

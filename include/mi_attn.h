@@ -30,12 +30,19 @@ typedef enum {
   ATTN_OK = 0,
   ATTN_ERR_NULL = -1,      /* a required pointer (q, k, v, o, lse, or an out-param) is NULL */
   ATTN_ERR_SHAPE = -2,     /* a size is negative, or one head (N*d*2 bytes) reaches 2^31 */
-  ATTN_ERR_HEADDIM = -3,   /* d is neither 64 nor 128 */
+  ATTN_ERR_HEADDIM = -3,   /* d is not one of 32, 64, 128, 256 */
   ATTN_ERR_ALIGN = -5,     /* q, k, v or o not 16-byte aligned, or lse not 4-byte aligned */
   ATTN_ERR_ALIAS = -6,     /* o or lse overlaps an input, or o overlaps lse */
   ATTN_ERR_SCALE = -7,     /* scale is NaN or infinite */
-  ATTN_ERR_LAUNCH = -8     /* the HIP launch failed (no gfx950 device, bad stream, ...) */
+  ATTN_ERR_LAUNCH = -8,    /* the HIP launch failed (no gfx950 device, bad stream, ...) */
+  ATTN_ERR_DTYPE = -9      /* dtype is not an attn_dtype value */
 } attn_status;
+
+/* Element type of q, k, v and o (attn_fwd_ex). lse is always float32. */
+typedef enum {
+  ATTN_BF16 = 0,  /* bfloat16: 8-bit exponent, 8-bit significand */
+  ATTN_F16 = 1    /* IEEE binary16: 5-bit exponent, 11-bit significand */
+} attn_dtype;
 
 /*
  * attn_fwd - attention forward with per-row log-sum-exp.
@@ -47,7 +54,7 @@ typedef enum {
  *   B, H, N  batch size, heads, sequence length (queries and keys share N).
  *            Any N >= 1 is accepted (no multiple-of-tile restriction). If
  *            B*H*N == 0 the call does nothing and returns ATTN_OK.
- *   d        head dimension: 64 or 128.
+ *   d        head dimension: 32, 64, 128 or 256.
  *   scale    softmax scale, applied to Q K^T before masking; used exactly as
  *            the given float32 value. Any finite value (0 and negative
  *            included) is accepted.
@@ -87,6 +94,18 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 int attn_fwd_cross(const void* q, const void* k, const void* v, void* o, float* lse,
                    int B, int H, int Nq, int Nk, int d, float scale, int causal,
                    void* stream);
+
+/*
+ * attn_fwd_ex - attn_fwd_cross with the element type of q, k, v and o chosen
+ * by `dtype` (an attn_dtype: ATTN_BF16 or ATTN_F16; anything else returns
+ * ATTN_ERR_DTYPE before any HIP call). With ATTN_F16 the softmax weights are
+ * rounded to fp16 before the P*V product and o is written in fp16 (nearest
+ * even); everything else is as for attn_fwd_cross.
+ * attn_fwd_cross(...) == attn_fwd_ex(..., d, ATTN_BF16, scale, causal, stream).
+ */
+int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+                int B, int H, int Nq, int Nk, int d, int dtype, float scale, int causal,
+                void* stream);
 
 /* attn_strerror - static, NUL-terminated description of a status code
  * (an unknown code yields "unknown status"). Never NULL. */

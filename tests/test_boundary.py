@@ -18,6 +18,7 @@ HEADER = os.path.join(ROOT, "include", "mi_attn.h")
 
 OK, ERR_NULL, ERR_SHAPE, ERR_HEADDIM, ERR_ALIGN, ERR_ALIAS, ERR_SCALE, ERR_LAUNCH = (
     0, -1, -2, -3, -5, -6, -7, -8)
+ERR_DTYPE = -9
 
 MIB = 1 << 20
 # Stand-in device addresses, 1 MiB apart and 256-byte aligned.
@@ -39,8 +40,8 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["attn_fwd", "attn_fwd_cross", "attn_fwd_launch_shape",
-                                    "attn_strerror"]
+    assert declared_functions() == ["attn_fwd", "attn_fwd_cross", "attn_fwd_ex",
+                                    "attn_fwd_launch_shape", "attn_strerror"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -65,11 +66,11 @@ def test_no_extra_exported_c_symbols():
 def test_strerror_covers_every_status(lib):
     seen = set()
     for code in (OK, ERR_NULL, ERR_SHAPE, ERR_HEADDIM, ERR_ALIGN, ERR_ALIAS,
-                 ERR_SCALE, ERR_LAUNCH):
+                 ERR_SCALE, ERR_LAUNCH, ERR_DTYPE):
         msg = mi.attn_strerror(code)
         assert msg and msg != "unknown status"
         seen.add(msg)
-    assert len(seen) == 8
+    assert len(seen) == 9
     assert mi.attn_strerror(12345) == "unknown status"
 
 
@@ -93,7 +94,7 @@ def test_size_overflow(lib):
     assert call(lib, B=big, H=big, N=big, d=128) == ERR_SHAPE
 
 
-@pytest.mark.parametrize("d", [0, 1, 16, 32, 63, 65, 96, 127, 129, 256])
+@pytest.mark.parametrize("d", [0, 1, 16, 31, 63, 65, 96, 127, 129, 255, 512])
 def test_unsupported_head_dim(lib, d):
     assert call(lib, d=d) == ERR_HEADDIM
 
@@ -142,7 +143,7 @@ def test_validation_order(lib):
 @pytest.mark.parametrize("B,H,N,d,causal", [
     (1, 1, 128, 64, 0), (4, 16, 1024, 64, 0), (8, 16, 2048, 64, 1),
     (16, 16, 4096, 128, 0), (1, 32, 16384, 128, 1), (2, 3, 1, 64, 0),
-    (2, 3, 129, 128, 1)])
+    (2, 3, 129, 128, 1), (2, 3, 500, 32, 0), (1, 2, 300, 256, 1)])
 def test_launch_shape(lib, B, H, N, d, causal):
     s = mi.attn_fwd_launch_shape(B, H, N, d, causal)
     bm = s["block_m"]
@@ -205,3 +206,35 @@ def test_cross_aliasing_uses_each_tensors_size(lib):
 def test_cross_headdim_and_scale(lib):
     assert cross(lib, d=96) == ERR_HEADDIM
     assert cross(lib, scale=float("nan")) == ERR_SCALE
+
+
+# ---------------------------------------------------------- attn_fwd_ex --
+
+def ex(lib, dtype=0, d=128, **kw):
+    args = dict(q=Q, k=K, v=V, o=O, lse=L, B=2, H=3, Nq=100, Nk=70, scale=0.125, causal=0)
+    args.update(kw)
+    return lib.attn_fwd_ex(args["q"], args["k"], args["v"], args["o"], args["lse"], args["B"],
+                           args["H"], args["Nq"], args["Nk"], d, dtype, args["scale"],
+                           args["causal"], None)
+
+
+@pytest.mark.parametrize("dtype", [-1, 2, 7])
+def test_ex_rejects_unknown_dtype(lib, dtype):
+    assert ex(lib, dtype=dtype) == ERR_DTYPE
+
+
+@pytest.mark.parametrize("dtype", [0, 1])
+def test_ex_validates_like_the_others(lib, dtype):
+    assert ex(lib, dtype=dtype, d=96) == ERR_HEADDIM
+    assert ex(lib, dtype=dtype, q=None) == ERR_NULL
+    assert ex(lib, dtype=dtype, o=Q) == ERR_ALIAS
+    assert ex(lib, dtype=dtype, Nq=0, q=None, o=None, lse=None) == OK
+
+
+def test_binding_dtype_rules():
+    import torch
+    q = torch.zeros(1, 1, 8, 64, dtype=torch.float16)
+    with pytest.raises(TypeError):  # attn_fwd is bf16 only
+        mi.attn_fwd(q, q, q)
+    with pytest.raises(TypeError):  # mixed dtypes
+        mi.attn_fwd_ex(q, q.to(torch.bfloat16), q)

@@ -307,3 +307,114 @@ def test_hand_examples_on_gpu():
         fin = np.isfinite(c["lse"])
         assert np.allclose(o[0, 0, :, :nd], c["O"], atol=0.05)
         assert np.allclose(lse[0, 0][fin], c["lse"][fin], atol=0.05)
+
+
+# ------------------------------------------- float16 and head dims 32, 256 --
+
+DTYPES = {"bf16": torch.bfloat16, "f16": torch.float16}
+
+
+def run_ex(q, k, v, scale, causal):
+    dev = torch.device("cuda:0")
+    o, lse = mi.attn_fwd_ex(q.to(dev), k.to(dev), v.to(dev), scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    assert o.dtype == q.dtype
+    return o.float().cpu().numpy(), lse.cpu().numpy()
+
+
+EX_SELF = [(1, 1, 1), (1, 2, 17), (2, 3, 100), (1, 1, 129), (2, 2, 300), (1, 3, 513),
+           (1, 1, 1000)]
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+@pytest.mark.parametrize("d", [32, 64, 128, 256])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("B,H,N", EX_SELF)
+def test_ex_self(B, H, N, d, causal, dt):
+    """Every head dim in both element types, Nq == Nk, ragged N."""
+    announce(f"ex self B={B} H={H} N={N} d={d} causal={causal} {dt}")
+    inp = make_inputs(WORKLOADS[1], B=B, H=H, N=N, d=d, seed=4000 + N + d, dtype=DTYPES[dt])
+    o, lse = run_ex(inp["q"], inp["k"], inp["v"], inp["scale"], causal)
+    o_ref, lse_ref = attention_ref(as64(inp["q"]), as64(inp["k"]), as64(inp["v"]),
+                                   inp["scale"], causal)
+    check(o, lse, o_ref, lse_ref, f"N={N} d={d} causal={causal} {dt}")
+
+
+EX_CROSS = [(1, 1), (3, 2), (100, 37), (37, 100), (129, 1000), (1000, 129), (200, 1)]
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+@pytest.mark.parametrize("d", [32, 256])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("Nq,Nk", EX_CROSS)
+def test_ex_cross(Nq, Nk, d, causal, dt):
+    announce(f"ex cross Nq={Nq} Nk={Nk} d={d} causal={causal} {dt}")
+    qi = make_inputs(WORKLOADS[1], B=2, H=2, N=Nq, d=d, seed=5000 + Nq, dtype=DTYPES[dt])
+    ki = make_inputs(WORKLOADS[1], B=2, H=2, N=Nk, d=d, seed=6000 + Nk, dtype=DTYPES[dt])
+    o, lse = run_ex(qi["q"], ki["k"], ki["v"], qi["scale"], causal)
+    o_ref, lse_ref = attention_ref(as64(qi["q"]), as64(ki["k"]), as64(ki["v"]),
+                                   qi["scale"], causal)
+    check_with_empty_rows(o, lse, o_ref, lse_ref, f"cross {Nq}x{Nk} d={d} {dt}")
+
+
+@pytest.mark.parametrize("d", [32, 256])
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_ex_without_keys(d, dt):
+    announce(f"ex Nk=0 d={d} {dt}")
+    dev = torch.device("cuda:0")
+    q = torch.randn(1, 2, 70, d).to(DTYPES[dt]).to(dev)
+    k = torch.zeros(1, 2, 0, d, dtype=DTYPES[dt], device=dev)
+    o, lse = mi.attn_fwd_ex(q, k, k, causal=True)
+    torch.cuda.synchronize()
+    assert bool((o == 0).all()) and bool(torch.isneginf(lse).all())
+
+
+def test_ex_bf16_is_attn_fwd_cross():
+    """The bf16 path of attn_fwd_ex is the kernel attn_fwd_cross runs."""
+    announce("ex bf16 == cross")
+    qi = make_inputs(WORKLOADS[3], B=1, H=2, N=300, d=128, seed=15)
+    ki = make_inputs(WORKLOADS[3], B=1, H=2, N=170, d=128, seed=16)
+    dev = torch.device("cuda:0")
+    q, k, v = qi["q"].to(dev), ki["k"].to(dev), ki["v"].to(dev)
+    for causal in (False, True):
+        o1, l1 = mi.attn_fwd_cross(q, k, v, causal=causal)
+        o2, l2 = mi.attn_fwd_ex(q, k, v, causal=causal)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+@pytest.mark.parametrize("d", [32, 256])
+def test_ex_zero_query_gives_mean_of_visible_values(d, dt):
+    """q = 0: every visible key has weight 1/count, so O is a running mean of
+    V and lse = ln(count), at any size."""
+    announce(f"ex zero query d={d} {dt}")
+    N = 777
+    dev = torch.device("cuda:0")
+    g = torch.Generator("cpu").manual_seed(d)
+    v = torch.randn(1, 2, N, d, generator=g).to(DTYPES[dt])
+    k = torch.randn(1, 2, N, d, generator=g).to(DTYPES[dt])
+    q = torch.zeros(1, 2, N, d, dtype=DTYPES[dt])
+    o, lse = run_ex(q, k, v, 0.3, True)
+    cnt = np.arange(1, N + 1, dtype=np.float64)
+    mean = np.cumsum(as64(v), axis=2) / cnt[None, None, :, None]
+    check(o, lse, mean, np.broadcast_to(np.log(cnt), lse.shape), f"zero query d={d} {dt}")
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+@pytest.mark.parametrize("d,N,causal", [(32, 16384, True), (256, 8192, False),
+                                        (256, 8192, True)])
+def test_ex_long_sampled(d, N, causal, dt):
+    """Long sequences at the new head dims: 48 sampled rows per head (the first,
+    the last, and rows around tile edges) against the oracle row by row."""
+    announce(f"ex long d={d} N={N} causal={causal} {dt}")
+    inp = make_inputs(WORKLOADS[4], B=1, H=4, N=N, d=d, seed=7000 + d, dtype=DTYPES[dt])
+    o, lse = run_ex(inp["q"], inp["k"], inp["v"], inp["scale"], causal)
+    rng = np.random.default_rng(d + N)
+    rows = np.unique(np.concatenate([[0, 1, 127, 128, N - 129, N - 1],
+                                     rng.integers(0, N, 42)]))
+    q64, k64, v64 = as64(inp["q"]), as64(inp["k"]), as64(inp["v"])
+    for h in range(4):
+        o_ref, lse_ref = attend_head(q64[0, h, rows], k64[0, h], v64[0, h], inp["scale"],
+                                     causal, q_pos=rows)
+        check(o[0, h, rows], lse[0, h, rows], o_ref, lse_ref, f"head {h}")

@@ -13,8 +13,11 @@ import ctypes
 import math
 import os
 
-__all__ = ["attn_fwd", "attn_fwd_cross", "attn_strerror", "attn_fwd_launch_shape",
-           "lib_path", "load_library", "AttnError"]
+__all__ = ["attn_fwd", "attn_fwd_cross", "attn_fwd_ex", "attn_strerror",
+           "attn_fwd_launch_shape", "lib_path", "load_library", "AttnError", "ATTN_BF16",
+           "ATTN_F16"]
+
+ATTN_BF16, ATTN_F16 = 0, 1  # attn_dtype values of the C ABI
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmi_attn.so")
 _lib = None
@@ -47,6 +50,8 @@ def load_library():
     lib.attn_fwd.restype = i32
     lib.attn_fwd_cross.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp]
     lib.attn_fwd_cross.restype = i32
+    lib.attn_fwd_ex.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, vp]
+    lib.attn_fwd_ex.restype = i32
     lib.attn_strerror.argtypes = [i32]
     lib.attn_strerror.restype = ctypes.c_char_p
     ip = ctypes.POINTER(i32)
@@ -72,14 +77,18 @@ def attn_fwd_launch_shape(B, H, N, d, causal=False):
                     (x.value for x in out)))
 
 
-def _check_inputs(q, k, v):
+def _check_inputs(q, k, v, dtypes=None):
     import torch
 
+    dtypes = (torch.bfloat16,) if dtypes is None else dtypes
     for name, t in (("q", q), ("k", k), ("v", v)):
         if not isinstance(t, torch.Tensor):
             raise TypeError(f"{name} must be a torch.Tensor")
-        if t.dtype != torch.bfloat16:
-            raise TypeError(f"{name} must be bfloat16, got {t.dtype}")
+        if t.dtype not in dtypes:
+            raise TypeError(f"{name} must be one of {dtypes}, got {t.dtype}")
+        if t.dtype != q.dtype:
+            raise TypeError("q, k, v must share one dtype")
+    for name, t in (("q", q), ("k", k), ("v", v)):
         if t.device.type != "cuda":
             raise ValueError(f"{name} must be on a HIP device, got {t.device}")
         if not t.is_contiguous():
@@ -99,9 +108,9 @@ def _outputs(q, out, lse):
     B, H, Nq, _ = q.shape
     if out is None:
         out = torch.empty_like(q)
-    elif (out.shape != q.shape or out.dtype != torch.bfloat16
+    elif (out.shape != q.shape or out.dtype != q.dtype
           or out.device != q.device or not out.is_contiguous()):
-        raise ValueError("out must be a contiguous bf16 tensor shaped like q")
+        raise ValueError("out must be a contiguous tensor shaped like q, of q's dtype")
     if lse is None:
         lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
     elif (tuple(lse.shape) != (B, H, Nq) or lse.dtype != torch.float32
@@ -172,6 +181,29 @@ def attn_fwd_cross(q, k, v, scale=None, causal=False, out=None, lse=None, stream
         rc = lib.attn_fwd_cross(q.data_ptr(), kp, vp, out.data_ptr(), lse.data_ptr(),
                                 B, H, Nq, Nk, d, float(scale), int(bool(causal)),
                                 _stream_handle(q, stream))
+    if rc:
+        raise AttnError(rc, attn_strerror(rc))
+    return out, lse
+
+
+def attn_fwd_ex(q, k, v, scale=None, causal=False, out=None, lse=None, stream=None):
+    """attn_fwd_cross for bfloat16 or float16 tensors (q, k, v one dtype; o
+    gets that dtype, lse float32)."""
+    import torch
+
+    lib = load_library()
+    _check_inputs(q, k, v, dtypes=(torch.bfloat16, torch.float16))
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    dtype = ATTN_BF16 if q.dtype == torch.bfloat16 else ATTN_F16
+    scale = _default_scale(d) if scale is None else scale
+    out, lse = _outputs(q, out, lse)
+    kp = k.data_ptr() if Nk else 0
+    vp = v.data_ptr() if Nk else 0
+    with torch.cuda.device(q.device):
+        rc = lib.attn_fwd_ex(q.data_ptr(), kp, vp, out.data_ptr(), lse.data_ptr(), B, H, Nq,
+                             Nk, d, dtype, float(scale), int(bool(causal)),
+                             _stream_handle(q, stream))
     if rc:
         raise AttnError(rc, attn_strerror(rc))
     return out, lse

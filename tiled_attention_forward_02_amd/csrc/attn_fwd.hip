@@ -58,10 +58,33 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// The two 16-bit input types: 8-element MFMA operands, the 32x32x16 MFMA
+// with fp32 accumulation, and rounding from fp32 (to nearest even).
+template <typename E>
+struct Elem;
+template <>
+struct Elem<__bf16> {
+  typedef bf16x8 v8;
+  typedef bf16x4 v4;
+  static __device__ __forceinline__ f32x16 mfma(v8 a, v8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+};
+template <>
+struct Elem<_Float16> {
+  typedef f16x8 v8;
+  typedef f16x4 v4;
+  static __device__ __forceinline__ f32x16 mfma(v8 a, v8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+};
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -71,7 +94,7 @@ constexpr float kLazySum = 4096.f;  // largest per-lane tile sum kept on a stale
 // where the 32-key tile's scores are cheap to keep live) or row maximum
 // first (d=64, where keeping 64 scores live would cost a wave per SIMD).
 template <int D>
-constexpr bool kSpeculativeWeights = D == 128;
+constexpr bool kSpeculativeWeights = D >= 128;
 
 constexpr int kWaves = 4;              // waves per workgroup
 constexpr int kThreads = 64 * kWaves;  // threads per workgroup
@@ -82,7 +105,11 @@ constexpr int kBlockM = 32 * kWaves;   // query rows per workgroup
 template <int D>
 constexpr int kBlockN = 64;
 template <>
+constexpr int kBlockN<32> = 128;  // each thread still stages 2 keys of 8 columns
+template <>
 constexpr int kBlockN<128> = 32;
+template <>
+constexpr int kBlockN<256> = 32;
 
 // Per head dimension D and tile width BN: the key tile and its LDS layout.
 template <int D, int BN_>
@@ -94,10 +121,15 @@ struct Tile {
   static constexpr int VT_ELEMS = D * BN;        // one V^T tile
   static constexpr int CPR = D / 8;              // 16-byte chunks per row
   static constexpr int KPT = BN * CPR / kThreads;  // rows each thread stages (4 or 2)
+  // V staging: key groups of KPT keys spread over VG consecutive lanes (16,
+  // or fewer when the tile has fewer groups), then the 16-byte chunk.
+  static constexpr int VG = BN / KPT < 16 ? BN / KPT : 16;
   static constexpr int STAGE = K_ELEMS + VT_ELEMS;
   static constexpr int LDS_ELEMS = 2 * STAGE;
   static constexpr int LDS_BYTES = 2 * LDS_ELEMS;
   static_assert(KPT == 2 || KPT == 4, "staging layout");
+  static_assert(BN % (VG * KPT) == 0 && VG * CPR * (BN / (VG * KPT)) == kThreads,
+                "V staging covers the tile exactly once");
 };
 
 // Key order inside a 16-key slice of V^T in LDS: swaps bits 2 and 3 of the
@@ -114,7 +146,7 @@ __device__ __forceinline__ int slice_pos(int o) {
 template <int BN>
 __device__ __forceinline__ int vt_swz(int d) {
   d &= 31;
-  return BN == 64 ? ((d ^ (d >> 3)) & 7) : (((d >> 1) ^ (d >> 3)) & 3);
+  return BN >= 64 ? ((d ^ (d >> 3)) & 7) : (((d >> 1) ^ (d >> 3)) & 3);
 }
 
 // Workgroup id -> (batch*head, query tile). Workgroups are dealt to the 8
@@ -167,14 +199,16 @@ __device__ __forceinline__ float swap_halves_add(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, kBlockN<D> == 32 ? 3 : 2) void attn_fwd_kernel(
-    const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
-    const __bf16* __restrict__ V, __bf16* __restrict__ O,
+template <typename E, int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, D == 256 ? 1 : D == 128 ? 3 : 2) void attn_fwd_kernel(
+    const E* __restrict__ Q, const E* __restrict__ K,
+    const E* __restrict__ V, E* __restrict__ O,
     float* __restrict__ LSE, int BH, int Nq, int Nk, int nq, float c) {
   using T = Tile<D, kBlockN<D>>;
   constexpr int BN = T::BN, KS = T::KS, CPR = T::CPR, KPT = T::KPT, NKB = T::NKB;
-  __shared__ __attribute__((aligned(16))) __bf16 smem[T::LDS_ELEMS];
+  typedef typename Elem<E>::v8 v8;
+  typedef typename Elem<E>::v4 v4;
+  __shared__ __attribute__((aligned(16))) E smem[T::LDS_ELEMS];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, col = lane & 31, half = lane >> 5;
@@ -213,9 +247,9 @@ __global__ __launch_bounds__(kThreads, kBlockN<D> == 32 ? 3 : 2) void attn_fwd_k
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) qraw[s] = u32x4{0, 0, 0, 0};
   }
-  bf16x8 qf[D / 16];
+  v8 qf[D / 16];
 #pragma unroll
-  for (int s = 0; s < D / 16; ++s) qf[s] = __builtin_bit_cast(bf16x8, qraw[s]);
+  for (int s = 0; s < D / 16; ++s) qf[s] = __builtin_bit_cast(v8, qraw[s]);
 
   // Keys this workgroup / this wave can see.
   // Keys this workgroup / this wave can see (none for rows before -off).
@@ -224,14 +258,16 @@ __global__ __launch_bounds__(kThreads, kBlockN<D> == 32 ? 3 : 2) void attn_fwd_k
   const int wave_kv_end = CAUSAL ? min(Nk, qw + 32 + off) : Nk;
 
   // Staging. K: thread owns rows kr_k .. +KPT-1, 16-byte chunk dc_k, with the
-  // chunk fastest across lanes (whole rows per 16 lanes: coalesced loads,
-  // contiguous LDS writes). V: the key group fastest across lanes, so the 16
-  // lanes of one transposed LDS write cover 16 different key groups of one
-  // column (distinct banks) and each load still reads 64 contiguous bytes.
+  // chunk fastest across lanes (a row per CPR lanes: coalesced loads,
+  // contiguous LDS writes). V: the key group fastest across lanes, so the VG
+  // lanes of one transposed LDS write cover VG different key groups of one
+  // column (distinct banks) and a wave's load still reads 64/VG adjacent
+  // chunks (1024/VG contiguous bytes) of each row it touches.
+  constexpr int VG = T::VG;
   const int kr_k = KPT * (tid / CPR);
   const int dc_k = tid % CPR;
-  const int kr_v = KPT * (tid % 16) + 16 * KPT * (tid / (16 * CPR));
-  const int dc_v = (tid / 16) % CPR;
+  const int kr_v = KPT * (tid % VG) + VG * KPT * (tid / (VG * CPR));
+  const int dc_v = (tid / VG) % CPR;
   const uint32_t koff = (uint32_t)(kr_k * D + 8 * dc_k) * 2;
   const uint32_t voff = (uint32_t)(kr_v * D + 8 * dc_v) * 2;
   u32x4 kst[KPT], vst[KPT];
@@ -247,11 +283,11 @@ __global__ __launch_bounds__(kThreads, kBlockN<D> == 32 ? 3 : 2) void attn_fwd_k
   // Per-lane LDS byte offsets that do not change with the tile.
   const uint32_t k_wr = (uint32_t)(kr_k * KS + 8 * dc_k) * 2;
   const int vpos = 16 * (kr_v >> 4) + slice_pos(kr_v & 15);
-  // With 64-byte V^T rows (32-key tiles), odd 16-lane groups write the
-  // chunk's columns in the order e ^ 1, so the two groups that share an LDS
-  // cycle write rows of opposite parity instead of the same banks (measured:
-  // a third fewer bank-conflict cycles).
-  const int vflip = BN == 32 ? (tid >> 4) & 1 : 0;
+  // With 64-byte V^T rows (32-key tiles), odd VG-lane groups write the
+  // chunk's columns in the order e ^ 1, so neighbouring groups write rows of
+  // opposite parity instead of the same banks (measured at d=128: a third
+  // fewer bank-conflict cycles).
+  const int vflip = BN == 32 ? (tid / VG) & 1 : 0;
   uint32_t v_wr[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
@@ -314,9 +350,9 @@ __global__ __launch_bounds__(kThreads, kBlockN<D> == 32 ? 3 : 2) void attn_fwd_k
         sacc[kb] = f32x16{};
 #pragma unroll
         for (int j = 0; j < D / 16; ++j) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+          const v8 a = *reinterpret_cast<const v8*>(
               lds + base + k_rd + (32 * kb * KS + 16 * j) * 2);
-          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[j], sacc[kb], 0, 0, 0);
+          sacc[kb] = Elem<E>::mfma(a, qf[j], sacc[kb]);
         }
       }
 
@@ -332,7 +368,7 @@ __global__ __launch_bounds__(kThreads, kBlockN<D> == 32 ? 3 : 2) void attn_fwd_k
       }
 
       // P = 2^(s*c - m_run), rounded to bf16, and its row sum (fp32).
-      bf16x8 pb[NKB][2];
+      v8 pb[NKB][2];
       float tsum = 0.f;
       auto weights = [&]() __attribute__((always_inline)) {
         tsum = 0.f;
@@ -342,7 +378,7 @@ __global__ __launch_bounds__(kThreads, kBlockN<D> == 32 ? 3 : 2) void attn_fwd_k
           for (int i = 0; i < 16; ++i) {
             const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kb][i], c, -m_run));
             tsum += p;
-            pb[kb][i >> 3][i & 7] = (__bf16)p;
+            pb[kb][i >> 3][i & 7] = (E)p;
           }
       };
       // Row maximum of the tile in log2 units, both lane halves combined.
@@ -390,9 +426,9 @@ __global__ __launch_bounds__(kThreads, kBlockN<D> == 32 ? 3 : 2) void attn_fwd_k
         for (int sg = 0; sg < 2; ++sg) {
 #pragma unroll
           for (int db = 0; db < D / 32; ++db) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+            const v8 a = *reinterpret_cast<const v8*>(
                 lds + base + v_rd[2 * kb + sg] + 32 * db * BN * 2);
-            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kb][sg], oacc[db], 0, 0, 0);
+            oacc[db] = Elem<E>::mfma(a, pb[kb][sg], oacc[db]);
           }
         }
     }
@@ -419,10 +455,10 @@ __global__ __launch_bounds__(kThreads, kBlockN<D> == 32 ? 3 : 2) void attn_fwd_k
   for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      bf16x4 v4;
+      v4 o4;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v4[e] = (__bf16)(oacc[db][4 * r + e] * inv);
-      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v4), ro,
+      for (int e = 0; e < 4; ++e) o4[e] = (E)(oacc[db][4 * r + e] * inv);
+      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, o4), ro,
                                             (int)((qi * D + 32 * db + 8 * r + 4 * half) * 2),
                                             0, 0);
     }
@@ -440,21 +476,31 @@ struct Shape {
   int grid, block, lds, block_m, block_n, nq;
 };
 
+template <int D>
+void tile_info(Shape* sh) {
+  sh->lds = Tile<D, kBlockN<D>>::LDS_BYTES;
+  sh->block_n = kBlockN<D>;
+}
+
 // Sizes shared by every entry point; Nk only bounds the key tensors.
 int check_sizes(int B, int H, int Nq, int Nk, int d, Shape* sh) {
   if (B < 0 || H < 0 || Nq < 0 || Nk < 0) return ATTN_ERR_SHAPE;
-  if (d != 64 && d != 128) return ATTN_ERR_HEADDIM;
-  // One head's tensors are addressed with 32-bit byte offsets.
+  if (d != 32 && d != 64 && d != 128 && d != 256) return ATTN_ERR_HEADDIM;
+  // One head's tensors are addressed with 32-bit byte offsets (plus one tile).
   if ((int64_t)Nq * d * 2 + (int64_t)kBlockM * d * 2 > INT32_MAX) return ATTN_ERR_SHAPE;
-  if ((int64_t)Nk * d * 2 + (int64_t)kBlockN<64> * 128 * 2 > INT32_MAX) return ATTN_ERR_SHAPE;
+  if ((int64_t)Nk * d * 2 + (int64_t)128 * d * 2 > INT32_MAX) return ATTN_ERR_SHAPE;
   if ((int64_t)B * H > INT32_MAX) return ATTN_ERR_SHAPE;
   const int64_t nq = ((int64_t)Nq + kBlockM - 1) / kBlockM;
   const int64_t grid = (int64_t)B * H * nq;
   if (grid > INT32_MAX) return ATTN_ERR_SHAPE;
   sh->grid = (int)grid;
   sh->block = kThreads;
-  sh->lds = d == 64 ? Tile<64, kBlockN<64>>::LDS_BYTES : Tile<128, kBlockN<128>>::LDS_BYTES;
-  sh->block_n = d == 64 ? kBlockN<64> : kBlockN<128>;
+  switch (d) {
+    case 32: tile_info<32>(sh); break;
+    case 64: tile_info<64>(sh); break;
+    case 128: tile_info<128>(sh); break;
+    default: tile_info<256>(sh); break;
+  }
   sh->block_m = kBlockM;
   sh->nq = (int)nq;
   return ATTN_OK;
@@ -466,25 +512,46 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   return x < y + nb && y < x + na;
 }
 
-template <int D, bool CAUSAL>
-hipError_t launch(const Shape& sh, const void* q, const void* k, const void* v, void* o,
-                  float* lse, int BH, int Nq, int Nk, float c, hipStream_t stream) {
-  const __bf16* qp = static_cast<const __bf16*>(q);
-  const __bf16* kp = static_cast<const __bf16*>(k);
-  const __bf16* vp = static_cast<const __bf16*>(v);
-  __bf16* op = static_cast<__bf16*>(o);
-  int nq = sh.nq;
-  void* args[] = {&qp, &kp, &vp, &op, &lse, &BH, &Nq, &Nk, &nq, &c};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&attn_fwd_kernel<D, CAUSAL>),
-                         dim3(sh.grid), dim3(sh.block), args, 0, stream);
+struct Args {
+  const void *q, *k, *v;
+  void* o;
+  float* lse;
+  int BH, Nq, Nk;
+  float c;
+  hipStream_t stream;
+};
+
+template <typename E, int D, bool CAUSAL>
+hipError_t launch(const Shape& sh, const Args& a) {
+  const E* qp = static_cast<const E*>(a.q);
+  const E* kp = static_cast<const E*>(a.k);
+  const E* vp = static_cast<const E*>(a.v);
+  E* op = static_cast<E*>(a.o);
+  float* lp = a.lse;
+  int BH = a.BH, Nq = a.Nq, Nk = a.Nk, nq = sh.nq;
+  float c = a.c;
+  void* args[] = {&qp, &kp, &vp, &op, &lp, &BH, &Nq, &Nk, &nq, &c};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&attn_fwd_kernel<E, D, CAUSAL>),
+                         dim3(sh.grid), dim3(sh.block), args, 0, a.stream);
 }
 
-// Validation and launch behind attn_fwd and attn_fwd_cross.
+template <typename E>
+hipError_t launch_type(const Shape& sh, const Args& a, int d, bool causal) {
+  switch (d) {
+    case 32: return causal ? launch<E, 32, true>(sh, a) : launch<E, 32, false>(sh, a);
+    case 64: return causal ? launch<E, 64, true>(sh, a) : launch<E, 64, false>(sh, a);
+    case 128: return causal ? launch<E, 128, true>(sh, a) : launch<E, 128, false>(sh, a);
+    default: return causal ? launch<E, 256, true>(sh, a) : launch<E, 256, false>(sh, a);
+  }
+}
+
+// Validation and launch behind every attention entry point.
 int run(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
-        int Nq, int Nk, int d, float scale, int causal, void* stream) {
+        int Nq, int Nk, int d, int dtype, float scale, int causal, void* stream) {
   Shape sh;
   const int rc = check_sizes(B, H, Nq, Nk, d, &sh);
   if (rc != ATTN_OK) return rc;
+  if (dtype != ATTN_BF16 && dtype != ATTN_F16) return ATTN_ERR_DTYPE;
   uint32_t sbits;
   memcpy(&sbits, &scale, 4);
   if ((sbits & 0x7f800000u) == 0x7f800000u) return ATTN_ERR_SCALE;  // NaN or +-inf
@@ -501,17 +568,10 @@ int run(const void* q, const void* k, const void* v, void* o, float* lse, int B,
       overlaps(lse, lbytes, o, qbytes))
     return ATTN_ERR_ALIAS;
 
-  const float c = scale * kLog2e;
-  const int BH = B * H;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t err;
-  if (d == 64) {
-    err = causal ? launch<64, true>(sh, q, k, v, o, lse, BH, Nq, Nk, c, st)
-                 : launch<64, false>(sh, q, k, v, o, lse, BH, Nq, Nk, c, st);
-  } else {
-    err = causal ? launch<128, true>(sh, q, k, v, o, lse, BH, Nq, Nk, c, st)
-                 : launch<128, false>(sh, q, k, v, o, lse, BH, Nq, Nk, c, st);
-  }
+  const Args a{q, k, v, o, lse, B * H, Nq, Nk, scale * kLog2e,
+               static_cast<hipStream_t>(stream)};
+  const hipError_t err = dtype == ATTN_BF16 ? launch_type<__bf16>(sh, a, d, causal != 0)
+                                            : launch_type<_Float16>(sh, a, d, causal != 0);
   return err == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
@@ -520,13 +580,19 @@ int run(const void* q, const void* k, const void* v, void* o, float* lse, int B,
 extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                         int B, int H, int N, int d, float scale, int causal,
                         void* stream) {
-  return run(q, k, v, o, lse, B, H, N, N, d, scale, causal, stream);
+  return run(q, k, v, o, lse, B, H, N, N, d, ATTN_BF16, scale, causal, stream);
 }
 
 extern "C" int attn_fwd_cross(const void* q, const void* k, const void* v, void* o,
                               float* lse, int B, int H, int Nq, int Nk, int d, float scale,
                               int causal, void* stream) {
-  return run(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, stream);
+  return run(q, k, v, o, lse, B, H, Nq, Nk, d, ATTN_BF16, scale, causal, stream);
+}
+
+extern "C" int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int B, int H, int Nq, int Nk, int d, int dtype, float scale,
+                           int causal, void* stream) {
+  return run(q, k, v, o, lse, B, H, Nq, Nk, d, dtype, scale, causal, stream);
 }
 
 extern "C" const char* attn_strerror(int status) {
@@ -534,11 +600,12 @@ extern "C" const char* attn_strerror(int status) {
     case ATTN_OK: return "success";
     case ATTN_ERR_NULL: return "null pointer argument";
     case ATTN_ERR_SHAPE: return "invalid shape: sizes must be >= 0 and fit 32-bit head offsets";
-    case ATTN_ERR_HEADDIM: return "unsupported head dimension: d must be 64 or 128";
+    case ATTN_ERR_HEADDIM: return "unsupported head dimension: d must be 32, 64, 128 or 256";
     case ATTN_ERR_ALIGN: return "misaligned pointer: q, k, v, o need 16 bytes, lse 4 bytes";
     case ATTN_ERR_ALIAS: return "output buffer overlaps an input or the other output";
     case ATTN_ERR_SCALE: return "scale must be finite";
     case ATTN_ERR_LAUNCH: return "kernel launch failed";
+    case ATTN_ERR_DTYPE: return "unsupported element type: ATTN_BF16 or ATTN_F16";
     default: return "unknown status";
   }
 }

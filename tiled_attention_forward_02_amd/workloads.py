@@ -76,10 +76,11 @@ def attn_flops(B, H, N, d, causal):
 
 
 def make_inputs(w, B=None, H=None, N=None, d=None, seed=None, qk_std=None,
-                keep_fp32=False):
+                keep_fp32=False, dtype=torch.bfloat16):
     """Draw Q, K, V for workload ``w`` (sizes and seed may be overridden).
 
-    Returns a dict with bf16 CPU tensors ``q``, ``k``, ``v`` [B,H,N,d], the fp32
+    Returns a dict with CPU tensors ``q``, ``k``, ``v`` [B,H,N,d] rounded to
+    ``dtype`` (bf16 unless float16 is asked for), the fp32
     ``scale`` as a Python float, ``causal``, and with keep_fp32 the unrounded
     fp32 draws as ``q32``, ``k32``, ``v32``.
     """
@@ -98,9 +99,9 @@ def make_inputs(w, B=None, H=None, N=None, d=None, seed=None, qk_std=None,
         q32.mul_(qk_std)
         k32.mul_(qk_std)
     out = {
-        "q": q32.to(torch.bfloat16).contiguous(),
-        "k": k32.to(torch.bfloat16).contiguous(),
-        "v": v32.to(torch.bfloat16).contiguous(),
+        "q": q32.to(dtype).contiguous(),
+        "k": k32.to(dtype).contiguous(),
+        "v": v32.to(dtype).contiguous(),
         "scale": fp32_scale(d),
         "causal": w.causal,
     }
