@@ -30,13 +30,23 @@ Readings taken where the pages are silent (each is listed in the design notes):
 
 The score row is materialised in full (no online recurrence, no tiling), rows
 are processed in chunks only to bound memory.
+
+The backward (``attend_head_grad``) is the derivative of that same definition,
+written out with the chain rule; the pages call the FlashAttention backward
+much harder than the forward (Hacker News comments on the "GPUの爆発的な性能向上"
+page) and print nothing of it. For L = sum(dO * O), with P the softmax
+weights (masked entries 0):
+  dV = P^T dO;  dP = dO V^T;  dS = P * (dP - rowsum(P * dP));
+  dQ = scale * dS K;  dK = scale * dS^T Q.
+The last factor of dS is the Jacobian-vector product of a softmax row. A row
+that sees no key has P = 0 and contributes nothing.
 """
 
 from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["attend_head", "attention_ref"]
+__all__ = ["attend_head", "attention_ref", "attend_head_grad", "attention_grad_ref"]
 
 
 def attend_head(q, k, v, scale, causal, q_pos=None, return_weights=False,
@@ -111,3 +121,64 @@ def attention_ref(q, k, v, scale, causal):
         for h in range(h_n):
             o[b, h], lse[b, h] = attend_head(q[b, h], k[b, h], v[b, h], scale, causal)
     return o, lse
+
+
+def attend_head_grad(q, k, v, do, scale, causal, q_pos=None):
+    """Gradients of one head: returns (dq [M,d], dk [N,d], dv [N,d]) in float64,
+    of L = sum(do * o) with o the output of attend_head(q, k, v, scale, causal).
+
+    The weights are recomputed from the definition exactly as attend_head
+    forms them (full score matrix, masked entries -inf, max subtracted); then
+    the chain rule of the module docstring. q_pos as for attend_head.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    scale = float(scale)
+    m_rows, d = q.shape
+    n_keys = k.shape[0]
+    if k.shape != (n_keys, d) or v.shape[0] != n_keys or do.shape != (m_rows, v.shape[1]):
+        raise ValueError("q, k, v, do shapes do not agree")
+    if q_pos is None:
+        q_pos = np.arange(m_rows) + (n_keys - m_rows)
+    q_pos = np.asarray(q_pos, dtype=np.int64)
+
+    # softmax weights P [M, N]
+    s = scale * (q @ k.T)
+    if causal:
+        s[np.arange(n_keys)[None, :] > q_pos[:, None]] = -np.inf
+    if n_keys:
+        m = s.max(axis=1, keepdims=True)
+    else:
+        m = np.full((m_rows, 1), -np.inf)
+    empty = np.isneginf(m[:, 0])
+    m[empty] = 0.0
+    w = np.exp(s - m)
+    l = w.sum(axis=1, keepdims=True)
+    l[empty] = 1.0
+    p = w / l  # rows that see no key: all zero
+
+    dv = p.T @ do
+    dp = do @ v.T
+    ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+    dq = scale * (ds @ k)
+    dk = scale * (ds.T @ q)
+    return dq, dk, dv
+
+
+def attention_grad_ref(q, k, v, do, scale, causal):
+    """Gradients over a batch: q, do [B, H, M, d], k and v [B, H, N, d]; returns
+    (dq, dk, dv) in float64, each head handed to attend_head_grad."""
+    q, k, v, do = (np.asarray(t) for t in (q, k, v, do))
+    if (q.ndim != 4 or k.ndim != 4 or k.shape[:2] != q.shape[:2] or k.shape[3] != q.shape[3]
+            or v.shape[:3] != k.shape[:3] or do.shape != q.shape[:3] + (v.shape[3],)):
+        raise ValueError("expected q, do [B, H, M, d] and k, v [B, H, N, d]")
+    dq = np.empty(q.shape, dtype=np.float64)
+    dk = np.empty(k.shape, dtype=np.float64)
+    dv = np.empty(v.shape, dtype=np.float64)
+    for b in range(q.shape[0]):
+        for h in range(q.shape[1]):
+            dq[b, h], dk[b, h], dv[b, h] = attend_head_grad(q[b, h], k[b, h], v[b, h], do[b, h],
+                                                            scale, causal)
+    return dq, dk, dv
