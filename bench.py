@@ -1,7 +1,7 @@
 """Benchmark of the fused attention forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--head-dim D] [--dtype bf16|f16]
+                    [--head-dim D] [--dtype bf16|f16] [--pass fwd|bwd]
                     [--no-cpu-baseline] [--copy-calibration MIB]
 
 A step is one attn_fwd call over the whole workload (every query row of every
@@ -11,6 +11,12 @@ quoted on. --head-dim and --dtype keep the workload's B, H, N and causality
 and change the head dimension (32, 64, 128, 256) or the element type (float16
 goes through attn_fwd_ex); the workload name then carries the change. Prints
 ONE JSON line on stdout; diagnostics go to stderr.
+
+--pass bwd times attn_bwd instead (dq, dk, dv from o, lse of one forward
+call made before timing, and a seeded upstream gradient); its FLOP count is
+2.5x the forward's (five products of the same size as the forward's two:
+the score recomputation, dP, dV, dQ, dK), halved when causal, and its
+roofline covers the whole call (two kernels).
 
 FLOP per step follow the metric: 4*B*H*N^2*d, halved when causal.
 roofline.achieved = FLOP per launch / average launch duration, the duration
@@ -44,7 +50,9 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2516.6
 HBM_PEAK_GBS = 8000.0
 DEFAULT_WORKLOAD = "b16h16n4096d128"
-KERNEL_SRC = os.path.join(ROOT, "tiled_attention_forward_02_amd", "csrc", "attn_fwd.hip")
+CSRC = os.path.join(ROOT, "tiled_attention_forward_02_amd", "csrc")
+# The sources each timed pass is built from (hashed to tie profiles to code).
+KERNEL_SRCS = {"fwd": ("attn_fwd.hip", "common.h"), "bwd": ("attn_bwd.hip", "common.h")}
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -52,15 +60,18 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_sha():
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def kernel_sha(which="fwd"):
+    h = hashlib.sha256()
+    for name in KERNEL_SRCS[which]:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
-def stored_traffic(workload):
+def stored_traffic(workload, which="fwd"):
     """HBM bytes per launch from the committed counter summary, or None when
     it is missing or was taken on another version of the kernel source."""
-    path = os.path.join(PROFILES, f"attn_fwd_{workload}_hbm_traffic.txt")
+    path = os.path.join(PROFILES, f"attn_{which}_{workload}_hbm_traffic.txt")
     if not os.path.exists(path):
         return None
     fields = {}
@@ -68,7 +79,7 @@ def stored_traffic(workload):
         if ":" in line and not line.startswith("#"):
             key, val = line.split(":", 1)
             fields[key.strip()] = val.strip()
-    if fields.get("kernel_source_sha256_16") != kernel_sha():
+    if fields.get("kernel_source_sha256_16") != kernel_sha(which):
         return None
     try:
         return int(float(fields["hbm_bytes_per_launch"]))
@@ -76,13 +87,13 @@ def stored_traffic(workload):
         return None
 
 
-def cpu_baseline(w, inp, budget_s=15.0):
+def cpu_baseline(w, inp, budget_s=15.0, backward=False):
     """Time the fp64 oracle on whole heads of the same workload until about
-    budget_s seconds of CPU work are done; report it in the metric's unit."""
-    import numpy as np
+    budget_s seconds of CPU work are done; report it in the metric's unit
+    (backward: the oracle's gradients, on the backward's FLOP count)."""
     import torch
 
-    from oracle import attend_head
+    from oracle import attend_head, attend_head_grad
     try:
         from threadpoolctl import threadpool_info
         threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
@@ -92,22 +103,26 @@ def cpu_baseline(w, inp, budget_s=15.0):
     heads = [(b, h) for b in range(w.B) for h in range(w.H)]
     done = 0
     t0 = time.perf_counter()
+    f64 = lambda t: t.to(torch.float64).numpy()  # noqa: E731
     for b, h in heads:
-        attend_head(q[b, h].to(torch.float64).numpy(), k[b, h].to(torch.float64).numpy(),
-                    v[b, h].to(torch.float64).numpy(), inp["scale"], w.causal)
+        if backward:
+            attend_head_grad(f64(q[b, h]), f64(k[b, h]), f64(v[b, h]), f64(inp["do"][b, h]),
+                             inp["scale"], w.causal)
+        else:
+            attend_head(f64(q[b, h]), f64(k[b, h]), f64(v[b, h]), inp["scale"], w.causal)
         done += 1
         if time.perf_counter() - t0 >= budget_s:
             break
     dt = time.perf_counter() - t0
-    flops = done * 4.0 * w.N * w.N * w.d / (2 if w.causal else 1)
+    flops = done * (10.0 if backward else 4.0) * w.N * w.N * w.d / (2 if w.causal else 1)
     return {
         "value": flops / dt / 1e12,
         "unit": "TFLOP/s",
         "cores": int(threads),
         "kind": "oracle",
         "sample": f"{done} of {len(heads)} heads (N={w.N}, d={w.d}, "
-                  f"causal={w.causal}) in {dt:.1f} s, numpy fp64, "
-                  f"metric FLOP of those heads / wall time",
+                  f"causal={w.causal}){' gradients' if backward else ''} in {dt:.1f} s, "
+                  f"numpy fp64, metric FLOP of those heads / wall time",
     }
 
 
@@ -130,6 +145,25 @@ def parity_sample(w, inp, o, lse, rows=16):
     return {"max_abs_dO": eo, "max_abs_dlse": el, "ok": eo <= 2e-2 and el <= 1e-3}
 
 
+def parity_sample_bwd(w, inp, dq, rows=16):
+    """Sampled dq rows against the oracle (a row's dq needs only its own
+    weights) before timing the backward."""
+    import numpy as np
+    import torch
+
+    from oracle import attend_head_grad
+    rng = np.random.default_rng(8)
+    worst = 0.0
+    f64 = lambda t: t.to(torch.float64).numpy()  # noqa: E731
+    for b, h in ((0, 0), (w.B - 1, w.H - 1)):
+        r = np.sort(rng.choice(w.N, rows, replace=False))
+        ref, _, _ = attend_head_grad(f64(inp["q"][b, h][r]), f64(inp["k"][b, h]),
+                                     f64(inp["v"][b, h]), f64(inp["do"][b, h][r]),
+                                     inp["scale"], w.causal, q_pos=r)
+        worst = max(worst, float(np.abs(dq[b, h][r] - ref).max() / np.abs(ref).max()))
+    return {"max_abs_ddq_over_max_ref": worst, "ok": worst <= 2e-2}
+
+
 def copy_calibration(mib):
     import torch
     n = mib * (1 << 20)
@@ -150,6 +184,7 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--head-dim", type=int, default=0, choices=[0, 32, 64, 128, 256])
     ap.add_argument("--dtype", default="bf16", choices=["bf16", "f16"])
+    ap.add_argument("--pass", dest="which", default="fwd", choices=["fwd", "bwd"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
@@ -193,13 +228,31 @@ def main():
     log(f"launch: {shape}")
 
     fwd = mi.attn_fwd if args.dtype == "bf16" else mi.attn_fwd_ex
+    backward = args.which == "bwd"
 
     def step():
         fwd(q, k, v, scale=inp["scale"], causal=w.causal, out=o, lse=lse)
 
     step()
     torch.cuda.synchronize()
-    parity = parity_sample(w, inp, o.float().cpu().numpy(), lse.cpu().numpy())
+    if backward:
+        # o, lse of the forward above are the backward's inputs from here on.
+        g = torch.Generator("cpu").manual_seed(w.seed + 1000)
+        inp["do"] = torch.randn(q.shape, generator=g, dtype=torch.float32).to(elem)
+        do = inp["do"].to(dev)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        delta = torch.empty_like(lse)
+        w = dataclasses.replace(w, name=w.name + "_bwd")
+
+        def step():  # noqa: F811
+            mi.attn_bwd(q, k, v, o, lse, do, scale=inp["scale"], causal=w.causal, dq=dq, dk=dk,
+                        dv=dv, delta=delta)
+
+        step()
+        torch.cuda.synchronize()
+        parity = parity_sample_bwd(w, inp, dq.float().cpu().numpy())
+    else:
+        parity = parity_sample(w, inp, o.float().cpu().numpy(), lse.cpu().numpy())
     log(f"parity sample: {parity}")
     if not parity["ok"]:
         log("parity check failed; refusing to report a throughput")
@@ -222,20 +275,23 @@ def main():
     wall = time.perf_counter() - t0
     event_ms = ev0.elapsed_time(ev1)
 
-    flops = attn_flops(w.B, w.H, w.N, w.d, w.causal)
+    flops = attn_flops(w.B, w.H, w.N, w.d, w.causal) * (2.5 if backward else 1.0)
     launch_s = event_ms / 1e3 / args.steps
     achieved = flops / launch_s / 1e12
     value = flops * args.steps / wall / 1e12
-    traffic = stored_traffic(w.name)
+    traffic = stored_traffic(w.name, args.which)
     log(f"wall {wall*1e3:.2f} ms for {args.steps} steps; event avg {launch_s*1e6:.1f} us/launch")
 
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the oracle on the host cores ...")
-        cpu = cpu_baseline(w, inp, args.cpu_budget)
+        cpu = cpu_baseline(w, inp, args.cpu_budget, backward=backward)
 
+    metric = "attention fwd TFLOP/s and % of MI355X bf16 MFMA peak at d=64/128"
+    if backward:
+        metric = "attention bwd TFLOP/s (2.5x the forward's FLOP) and % of MI355X bf16 MFMA peak"
     line = {
-        "metric": "attention fwd TFLOP/s and % of MI355X bf16 MFMA peak at d=64/128",
+        "metric": metric,
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -260,7 +316,7 @@ def main():
         "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "kernel_avg_us": round(launch_s * 1e6, 2),
         "parity_sample": parity,
-        "kernel_source_sha256_16": kernel_sha(),
+        "kernel_source_sha256_16": kernel_sha(args.which),
     }
     print(json.dumps(line), flush=True)
 

@@ -1,5 +1,6 @@
 /*
- * mi_attn.h - C ABI of libmi_attn, a fused attention forward for MI355X (gfx950).
+ * mi_attn.h - C ABI of libmi_attn, a fused attention forward (and its
+ * gradients) for MI355X (gfx950).
  *
  * The operation (sources: "[GPU] Deep Learning for HPC", section "Flash
  * Attention" - scores Q K^T, softmax, times V, computed tile by tile without
@@ -30,7 +31,7 @@ typedef enum {
   ATTN_OK = 0,
   ATTN_ERR_NULL = -1,      /* a required pointer (q, k, v, o, lse, or an out-param) is NULL */
   ATTN_ERR_SHAPE = -2,     /* a size is negative, or one head (N*d*2 bytes) reaches 2^31 */
-  ATTN_ERR_HEADDIM = -3,   /* d is not one of 32, 64, 128, 256 */
+  ATTN_ERR_HEADDIM = -3,   /* d is not one of 32, 64, 128, 256 (attn_bwd: 64, 128) */
   ATTN_ERR_ALIGN = -5,     /* q, k, v or o not 16-byte aligned, or lse not 4-byte aligned */
   ATTN_ERR_ALIAS = -6,     /* o or lse overlaps an input, or o overlaps lse */
   ATTN_ERR_SCALE = -7,     /* scale is NaN or infinite */
@@ -106,6 +107,51 @@ int attn_fwd_cross(const void* q, const void* k, const void* v, void* o, float* 
 int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
                 int B, int H, int Nq, int Nk, int d, int dtype, float scale, int causal,
                 void* stream);
+
+/*
+ * attn_bwd - gradients of the attention forward: dq, dk, dv of the loss
+ * sum(d_o * o) for o = attn_fwd_ex(q, k, v, ..., scale, causal).
+ *
+ * The pages print no backward pass ("GPUの爆発的な性能向上": the Hacker News
+ * comments call it much harder than the forward); this is the chain rule of
+ * the forward definition above. With p_ij = exp(s_ij - lse_i) the softmax
+ * weights (0 for masked keys) and D_i = sum_c d_o_ic * o_ic:
+ *
+ *     dv_j  = sum_i p_ij d_o_i
+ *     ds_ij = p_ij (d_o_i . v_j - D_i)
+ *     dq_i  = scale * sum_j ds_ij k_j
+ *     dk_j  = scale * sum_i ds_ij q_i
+ *
+ * (D_i equals sum_j p_ij (d_o_i . v_j) because o_i = sum_j p_ij v_j.)
+ *
+ *   q, k, v   inputs of the forward: [B, H, Nq, d], [B, H, Nk, d], [B, H, Nk, d].
+ *   o, lse    the forward's outputs for exactly these q, k, v, scale, causal
+ *             ([B, H, Nq, d] and float32 [B, H, Nq]); p is recomputed from
+ *             lse, so an lse from other inputs gives meaningless gradients.
+ *             A row with lse = -inf (it saw no key) has p = 0.
+ *   d_o       upstream gradient [B, H, Nq, d].
+ *   dq        [B, H, Nq, d]; dk, dv [B, H, Nk, d]; written, every element.
+ *   delta     float32 [B, H, Nq], caller-owned; receives D_i (it is read back
+ *             by the second of the two kernels the call queues).
+ *   B, H, Nq, Nk, d, dtype, scale, causal, stream: as for attn_fwd_ex, except
+ *             that d must be 64 or 128.
+ *
+ * All tensors are contiguous row-major in the element type `dtype` (delta and
+ * lse float32). Arithmetic: products of the element type accumulated in fp32;
+ * p and ds rounded to the element type before the products that consume them;
+ * dq, dk, dv rounded to the element type (nearest even). No atomics: results
+ * are deterministic.
+ *
+ * Ownership and errors: as for attn_fwd. Pointers of a side with no rows may
+ * be NULL (Nq == 0: q, o, lse, d_o, dq, delta; Nk == 0: k, v, dk, dv); with
+ * Nq == 0, dk and dv are written as zeros; with Nk == 0, dq is zeros. dq, dk,
+ * dv and delta must not overlap any input or each other (ATTN_ERR_ALIAS).
+ * Alignment: 16 bytes for the element-type tensors, 4 for lse and delta. If
+ * B*H == 0 or Nq == Nk == 0 the call does nothing and returns ATTN_OK.
+ */
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+             const void* d_o, void* dq, void* dk, void* dv, float* delta, int B, int H,
+             int Nq, int Nk, int d, int dtype, float scale, int causal, void* stream);
 
 /* attn_strerror - static, NUL-terminated description of a status code
  * (an unknown code yields "unknown status"). Never NULL. */

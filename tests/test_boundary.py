@@ -40,7 +40,7 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["attn_fwd", "attn_fwd_cross", "attn_fwd_ex",
+    assert declared_functions() == ["attn_bwd", "attn_fwd", "attn_fwd_cross", "attn_fwd_ex",
                                     "attn_fwd_launch_shape", "attn_strerror"]
 
 
@@ -238,3 +238,46 @@ def test_binding_dtype_rules():
         mi.attn_fwd(q, q, q)
     with pytest.raises(TypeError):  # mixed dtypes
         mi.attn_fwd_ex(q, q.to(torch.bfloat16), q)
+
+
+# -------------------------------------------------------------- attn_bwd --
+# Fake, distinct, 16-byte aligned device addresses: validation happens before
+# any HIP call, so none of these is ever dereferenced.
+BQ_, BK_, BV_, BO_, BL_, BDO_, BDQ_, BDK_, BDV_, BDL_ = (0x100000 * (i + 1) for i in range(10))
+
+
+def bwd(lib, d=128, dtype=0, B=2, H=3, Nq=100, Nk=70, scale=0.125, causal=0, **ptrs):
+    p = dict(q=BQ_, k=BK_, v=BV_, o=BO_, lse=BL_, do=BDO_, dq=BDQ_, dk=BDK_, dv=BDV_, delta=BDL_)
+    p.update(ptrs)
+    return lib.attn_bwd(p["q"], p["k"], p["v"], p["o"], p["lse"], p["do"], p["dq"], p["dk"],
+                        p["dv"], p["delta"], B, H, Nq, Nk, d, dtype, scale, causal, None)
+
+
+@pytest.mark.parametrize("d", [0, 16, 32, 96, 256, 512])
+def test_bwd_head_dims(lib, d):
+    assert bwd(lib, d=d) == ERR_HEADDIM
+
+
+def test_bwd_rejects_bad_arguments(lib):
+    assert bwd(lib, dtype=2) == ERR_DTYPE
+    assert bwd(lib, scale=float("nan")) == ERR_SCALE
+    assert bwd(lib, Nq=-1) == ERR_SHAPE
+    assert bwd(lib, Nq=1 << 30) == ERR_SHAPE
+    for name in ("q", "k", "v", "o", "lse", "do", "dq", "dk", "dv", "delta"):
+        assert bwd(lib, **{name: None}) == ERR_NULL, name
+    assert bwd(lib, dk=BDQ_) == ERR_ALIAS      # two outputs on one buffer
+    assert bwd(lib, dv=BV_) == ERR_ALIAS       # output over an input
+    assert bwd(lib, delta=BL_) == ERR_ALIAS
+    assert bwd(lib, dq=BQ_ + 8) == ERR_ALIGN
+    assert bwd(lib, delta=BDL_ + 2) == ERR_ALIGN
+
+
+def test_bwd_empty_sides(lib):
+    # nothing to do: no launch, OK even with every pointer NULL
+    assert bwd(lib, B=0) == OK
+    assert bwd(lib, Nq=0, Nk=0, **{n: None for n in ("q", "k", "v", "o", "lse", "do", "dq",
+                                                      "dk", "dv", "delta")}) == OK
+    # a side with no rows may pass NULL for its own tensors (validation only here)
+    assert bwd(lib, Nq=0, q=None, o=None, lse=None, do=None, dq=None, delta=None,
+               k=None) == ERR_NULL
+    assert bwd(lib, Nk=0, k=None, v=None, dk=None, dv=None, q=None) == ERR_NULL

@@ -1,0 +1,246 @@
+"""Parity of the HIP attention backward against the fp64 oracle (GPU only).
+
+Each case runs the HIP forward (attn_fwd_ex) for o and lse, then attn_bwd,
+and compares dq, dk, dv with the oracle's gradients of the same rounded
+inputs. The bar, per gradient tensor X (bf16 or fp16 products, fp32
+accumulation; P, dS and the outputs rounded to the element type, each about
+2^-9 relative):
+
+    max |X - X_ref|  <= 2e-2 * max |X_ref| + 1e-5
+    ||X - X_ref||_F  <= 1e-2 * ||X_ref||_F + 1e-5 * sqrt(size)
+
+The 1e-5 floor covers gradients that vanish exactly (one visible key gives
+dS = P (dP - D) = 0, while the kernel's dP and D round differently in fp32).
+
+delta (the row sums of dO * O, fp32) is checked against the same sums of the
+GPU's own o, to 1e-5 relative. Every call goes through the C ABI (the ctypes
+binding); each GPU step prints its case first.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import tiled_attention_forward_02_amd as mi
+from oracle import attend_head_grad, attention_grad_ref
+from tiled_attention_forward_02_amd.workloads import WORKLOADS, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+MAX_TOL = 2e-2
+FRO_TOL = 1e-2
+ATOL = 1e-5
+DTYPES = {"bf16": torch.bfloat16, "f16": torch.float16}
+
+
+def announce(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no HIP device")
+    mi.load_library()
+
+
+def as64(t):
+    return t.to(torch.float64).numpy()
+
+
+def upstream(shape, seed, dtype):
+    g = torch.Generator("cpu").manual_seed(seed)
+    return torch.randn(shape, generator=g, dtype=torch.float32).to(dtype)
+
+
+def run(q, k, v, do, scale, causal):
+    """GPU forward then backward; returns numpy dq, dk, dv, delta, o."""
+    dev = torch.device("cuda:0")
+    q, k, v, do = (t.to(dev) for t in (q, k, v, do))
+    o, lse = mi.attn_fwd_ex(q, k, v, scale=scale, causal=causal)
+    delta = torch.empty(lse.shape, dtype=torch.float32, device=dev)
+    dq, dk, dv = mi.attn_bwd(q, k, v, o, lse, do, scale=scale, causal=causal, delta=delta)
+    torch.cuda.synchronize()
+    out = [t.float().cpu().numpy() for t in (dq, dk, dv)]
+    return out + [delta.cpu().numpy(), o.to(torch.float64).cpu().numpy()]
+
+
+def check_grad(got, ref, what):
+    assert np.all(np.isfinite(got)), f"{what}: non-finite gradient"
+    if ref.size == 0:
+        return
+    scale = float(np.abs(ref).max())
+    err = float(np.abs(got - ref).max())
+    fro = float(np.linalg.norm(got - ref))
+    fro_ref = float(np.linalg.norm(ref))
+    print(f"  {what}: max|err|={err:.3e} (max|ref|={scale:.3e}) fro={fro / max(fro_ref, 1e-300):.3e}",
+          flush=True)
+    assert err <= MAX_TOL * scale + ATOL, f"{what}: max error {err} vs max|ref| {scale}"
+    assert fro <= FRO_TOL * fro_ref + ATOL * np.sqrt(ref.size), \
+        f"{what}: Frobenius error {fro} vs {fro_ref}"
+
+
+def check_all(q, k, v, do, scale, causal, what):
+    dq, dk, dv, delta, o = run(q, k, v, do, scale, causal)
+    rq, rk, rv = attention_grad_ref(as64(q), as64(k), as64(v), as64(do), scale, causal)
+    check_grad(dq, rq, f"{what} dq")
+    check_grad(dk, rk, f"{what} dk")
+    check_grad(dv, rv, f"{what} dv")
+    ref_delta = (as64(do) * o).sum(-1)
+    assert np.allclose(delta, ref_delta, rtol=1e-5, atol=1e-5 * max(1.0, np.abs(ref_delta).max()))
+
+
+# ------------------------------------------------------------ ragged shapes --
+
+RAGGED = [(1, 1, 1), (1, 2, 17), (2, 3, 100), (1, 1, 129), (2, 2, 300), (1, 3, 513)]
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("B,H,N", RAGGED)
+def test_bwd_ragged(B, H, N, d, causal):
+    announce(f"bwd ragged B={B} H={H} N={N} d={d} causal={causal}")
+    inp = make_inputs(WORKLOADS[1], B=B, H=H, N=N, d=d, seed=8000 + N + d)
+    do = upstream(inp["q"].shape, 9000 + N + d, torch.bfloat16)
+    check_all(inp["q"], inp["k"], inp["v"], do, inp["scale"], causal, f"N={N} d={d}")
+
+
+CROSS = [(3, 2), (2, 3), (100, 37), (37, 100), (129, 1000), (1000, 129), (200, 1), (1, 200)]
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("Nq,Nk", CROSS)
+def test_bwd_cross(Nq, Nk, d, causal):
+    """Nq queries against Nk keys; causal rows that see no key get no gradient."""
+    announce(f"bwd cross Nq={Nq} Nk={Nk} d={d} causal={causal}")
+    qi = make_inputs(WORKLOADS[1], B=2, H=2, N=Nq, d=d, seed=10000 + Nq)
+    ki = make_inputs(WORKLOADS[1], B=2, H=2, N=Nk, d=d, seed=11000 + Nk)
+    do = upstream(qi["q"].shape, 12000 + Nq + Nk, torch.bfloat16)
+    check_all(qi["q"], ki["k"], ki["v"], do, qi["scale"], causal, f"cross {Nq}x{Nk}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [100, 300])
+def test_bwd_fp16(N, d, causal):
+    announce(f"bwd fp16 N={N} d={d} causal={causal}")
+    inp = make_inputs(WORKLOADS[1], B=2, H=2, N=N, d=d, seed=13000 + N + d,
+                      dtype=torch.float16)
+    do = upstream(inp["q"].shape, 14000 + N, torch.float16)
+    check_all(inp["q"], inp["k"], inp["v"], do, inp["scale"], causal, f"fp16 N={N} d={d}")
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.3, 0.9])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_other_scales(scale, causal):
+    announce(f"bwd scale={scale} causal={causal}")
+    inp = make_inputs(WORKLOADS[1], B=1, H=2, N=200, d=64, seed=15)
+    do = upstream(inp["q"].shape, 16, torch.bfloat16)
+    dq, dk, dv, _, _ = run(inp["q"], inp["k"], inp["v"], do, scale, causal)
+    rq, rk, rv = attention_grad_ref(as64(inp["q"]), as64(inp["k"]), as64(inp["v"]), as64(do),
+                                    scale, causal)
+    if scale == 0.0:
+        # uniform weights: dq = dk = 0 exactly
+        assert np.all(dq == 0) and np.all(dk == 0)
+    else:
+        check_grad(dq, rq, "dq")
+        check_grad(dk, rk, "dk")
+    check_grad(dv, rv, "dv")
+
+
+# --------------------------------------------------------------- edge cases --
+
+def test_bwd_one_side_empty():
+    announce("bwd Nq=0 and Nk=0")
+    dev = torch.device("cuda:0")
+    k = torch.randn(1, 2, 50, 64).to(torch.bfloat16).to(dev)
+    q0 = torch.zeros(1, 2, 0, 64, dtype=torch.bfloat16, device=dev)
+    lse0 = torch.zeros(1, 2, 0, dtype=torch.float32, device=dev)
+    dq, dk, dv = mi.attn_bwd(q0, k, k, q0, lse0, q0, causal=False)
+    torch.cuda.synchronize()
+    assert dq.numel() == 0 and bool((dk == 0).all()) and bool((dv == 0).all())
+    q = torch.randn(1, 2, 40, 64).to(torch.bfloat16).to(dev)
+    k0 = torch.zeros(1, 2, 0, 64, dtype=torch.bfloat16, device=dev)
+    o, lse = mi.attn_fwd_ex(q, k0, k0, causal=True)
+    do = torch.randn(1, 2, 40, 64).to(torch.bfloat16).to(dev)
+    dq, dk, dv = mi.attn_bwd(q, k0, k0, o, lse, do, causal=True)
+    torch.cuda.synchronize()
+    assert bool((dq == 0).all()) and dk.numel() == 0 and dv.numel() == 0
+
+
+def test_bwd_deterministic():
+    announce("bwd deterministic")
+    dev = torch.device("cuda:0")
+    inp = make_inputs(WORKLOADS[1], B=2, H=4, N=700, d=128, seed=17)
+    q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+    do = upstream(q.shape, 18, torch.bfloat16).to(dev)
+    o, lse = mi.attn_fwd_ex(q, k, v, causal=True)
+    a = mi.attn_bwd(q, k, v, o, lse, do, causal=True)
+    b = mi.attn_bwd(q, k, v, o, lse, do, causal=True)
+    torch.cuda.synchronize()
+    assert all(torch.equal(x, y) for x, y in zip(a, b))
+
+
+def test_bwd_non_default_stream_and_given_outputs():
+    announce("bwd side stream")
+    dev = torch.device("cuda:0")
+    inp = make_inputs(WORKLOADS[1], B=1, H=2, N=300, d=64, seed=19)
+    q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+    do = upstream(q.shape, 20, torch.bfloat16).to(dev)
+    o, lse = mi.attn_fwd_ex(q, k, v, causal=False)
+    ref = mi.attn_bwd(q, k, v, o, lse, do, causal=False)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    outs = [torch.full_like(q, 7.0), torch.full_like(k, 7.0), torch.full_like(v, 7.0)]
+    with torch.cuda.stream(s):
+        mi.attn_bwd(q, k, v, o, lse, do, causal=False, dq=outs[0], dk=outs[1], dv=outs[2],
+                    stream=s)
+    s.synchronize()
+    assert all(torch.equal(x, y) for x, y in zip(ref, outs))
+
+
+# ------------------------------------------------- the metric's workloads --
+
+@pytest.mark.parametrize("idx,heads", [(1, None), (2, None), (3, ((0, 0), (7, 15))),
+                                       (4, ((0, 0), (15, 15)))])
+def test_bwd_workloads(idx, heads):
+    """Full size on the GPU; every element of the listed heads (all heads when
+    None) against the oracle."""
+    w = WORKLOADS[idx - 1]
+    announce(f"bwd workload {w.name}")
+    inp = make_inputs(w)
+    do = upstream(inp["q"].shape, 20000 + idx, torch.bfloat16)
+    dq, dk, dv, delta, o = run(inp["q"], inp["k"], inp["v"], do, inp["scale"], w.causal)
+    q64, k64, v64, do64 = (as64(t) for t in (inp["q"], inp["k"], inp["v"], do))
+    heads = heads or [(b, h) for b in range(w.B) for h in range(w.H)]
+    for b, h in heads:
+        rq, rk, rv = attend_head_grad(q64[b, h], k64[b, h], v64[b, h], do64[b, h],
+                                      inp["scale"], w.causal)
+        check_grad(dq[b, h], rq, f"({b},{h}) dq")
+        check_grad(dk[b, h], rk, f"({b},{h}) dk")
+        check_grad(dv[b, h], rv, f"({b},{h}) dv")
+
+
+def test_bwd_long_causal_sampled():
+    """The long causal workload (B=1, H=32, N=16384, d=128) at full size: dq on
+    sampled rows against the oracle row by row (a row's dq needs only its own
+    weights), and for every head the identities that hold at any size:
+    sum_j dk_j = 0 and sum_j dv_j = sum_i do_i."""
+    w = WORKLOADS[4]
+    announce(f"bwd workload {w.name} (sampled)")
+    inp = make_inputs(w)
+    do = upstream(inp["q"].shape, 20005, torch.bfloat16)
+    dq, dk, dv, _, _ = run(inp["q"], inp["k"], inp["v"], do, inp["scale"], True)
+    q64, k64, v64, do64 = (as64(t) for t in (inp["q"], inp["k"], inp["v"], do))
+    rng = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([[0, 1, 31, 32, 127, 128, w.N - 1], rng.integers(0, w.N, 25)]))
+    for h in (0, 13, 31):
+        rq, _, _ = attend_head_grad(q64[0, h, rows], k64[0, h], v64[0, h], do64[0, h, rows],
+                                    inp["scale"], True, q_pos=rows)
+        check_grad(dq[0, h, rows], rq, f"head {h} dq rows")
+    # Each identity is compared with the size of the terms it sums.
+    dk64, dv64 = dk.astype(np.float64), dv.astype(np.float64)
+    assert np.abs(dk64.sum(axis=2)).max() <= 1e-2 * np.abs(dk64).sum(axis=2).max()
+    gap = np.abs(dv64.sum(axis=2) - do64.sum(axis=2)).max()
+    assert gap <= 1e-2 * max(np.abs(dv64).sum(axis=2).max(), np.abs(do64).sum(axis=2).max())

@@ -1,7 +1,7 @@
 """Python binding of libmi_attn: argument marshalling over the C ABI only.
 
-Every step of the attention forward runs in the HIP kernel behind
-``attn_fwd`` in libmi_attn.so; this module checks tensors, allocates the
+Every step of the attention forward and backward runs in the HIP kernels
+behind the C entry points of libmi_attn.so; this module checks tensors, allocates the
 outputs with torch (device memory and streams are all torch provides here) and
 passes raw pointers. There is no fallback: if the shared library is missing
 the first call raises.
@@ -13,7 +13,7 @@ import ctypes
 import math
 import os
 
-__all__ = ["attn_fwd", "attn_fwd_cross", "attn_fwd_ex", "attn_strerror",
+__all__ = ["attn_fwd", "attn_fwd_cross", "attn_fwd_ex", "attn_bwd", "attn_strerror",
            "attn_fwd_launch_shape", "lib_path", "load_library", "AttnError", "ATTN_BF16",
            "ATTN_F16"]
 
@@ -27,7 +27,7 @@ class AttnError(RuntimeError):
     """A non-zero status returned by libmi_attn."""
 
     def __init__(self, status, message):
-        super().__init__(f"attn_fwd failed ({status}): {message}")
+        super().__init__(f"libmi_attn call failed ({status}): {message}")
         self.status = status
 
 
@@ -52,6 +52,8 @@ def load_library():
     lib.attn_fwd_cross.restype = i32
     lib.attn_fwd_ex.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, vp]
     lib.attn_fwd_ex.restype = i32
+    lib.attn_bwd.argtypes = [vp] * 10 + [i32] * 6 + [f32, i32, vp]
+    lib.attn_bwd.restype = i32
     lib.attn_strerror.argtypes = [i32]
     lib.attn_strerror.restype = ctypes.c_char_p
     ip = ctypes.POINTER(i32)
@@ -207,3 +209,56 @@ def attn_fwd_ex(q, k, v, scale=None, causal=False, out=None, lse=None, stream=No
     if rc:
         raise AttnError(rc, attn_strerror(rc))
     return out, lse
+
+
+def _like(t, ref, shape, dtype, name):
+    """An output tensor: `t` checked, or a new one on ref's device."""
+    import torch
+
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=ref.device)
+    if (tuple(t.shape) != tuple(shape) or t.dtype != dtype or t.device != ref.device
+            or not t.is_contiguous()):
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor {tuple(shape)} on "
+                         f"{ref.device}")
+    return t
+
+
+def attn_bwd(q, k, v, o, lse, do, scale=None, causal=False, dq=None, dk=None, dv=None,
+             delta=None, stream=None):
+    """dq, dk, dv = gradients of sum(do * o) where o, lse = attn_fwd_ex(q, k, v,
+    scale, causal) are passed in (the forward's own outputs for these inputs).
+
+    q, o, do [B, H, Nq, d] and k, v [B, H, Nk, d] share one element type
+    (bf16 or fp16); lse is float32 [B, H, Nq]; d is 64 or 128. ``delta``
+    (float32 [B, H, Nq]) receives sum(do * o) per row and is allocated when
+    not given; dq, dk, dv may be given to write into. Queued on ``stream``
+    (default: torch's current stream of q's device); nothing synchronises.
+    """
+    import torch
+
+    lib = load_library()
+    _check_inputs(q, k, v, dtypes=(torch.bfloat16, torch.float16))
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    for name, t in (("o", o), ("do", do)):
+        if (not isinstance(t, torch.Tensor) or tuple(t.shape) != tuple(q.shape)
+                or t.dtype != q.dtype or t.device != q.device or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous tensor shaped like q, of q's dtype")
+    if (not isinstance(lse, torch.Tensor) or tuple(lse.shape) != (B, H, Nq)
+            or lse.dtype != torch.float32 or lse.device != q.device or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous float32 tensor [B, H, Nq]")
+    dq = _like(dq, q, q.shape, q.dtype, "dq")
+    dk = _like(dk, q, k.shape, q.dtype, "dk")
+    dv = _like(dv, q, k.shape, q.dtype, "dv")
+    delta = _like(delta, q, (B, H, Nq), torch.float32, "delta")
+    dtype = ATTN_BF16 if q.dtype == torch.bfloat16 else ATTN_F16
+    scale = _default_scale(d) if scale is None else scale
+    ptr = lambda t: t.data_ptr() if t.numel() else 0  # noqa: E731
+    with torch.cuda.device(q.device):
+        rc = lib.attn_bwd(ptr(q), ptr(k), ptr(v), ptr(o), ptr(lse), ptr(do), ptr(dq), ptr(dk),
+                          ptr(dv), ptr(delta), B, H, Nq, Nk, d, dtype, float(scale),
+                          int(bool(causal)), _stream_handle(q, stream))
+    if rc:
+        raise AttnError(rc, attn_strerror(rc))
+    return dq, dk, dv

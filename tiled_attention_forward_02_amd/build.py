@@ -13,7 +13,7 @@ import sys
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG_DIR)
-SRC = os.path.join(PKG_DIR, "csrc", "attn_fwd.hip")
+SRCS = [os.path.join(PKG_DIR, "csrc", f) for f in ("attn_fwd.hip", "attn_bwd.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG_DIR, "libmi_attn.so")
 ARCH = "gfx950"
@@ -34,12 +34,12 @@ def compile_command(out=LIB, extra=()):
         # NaN-free max/min on the device side only (no canonicalising moves)
         "-Xarch_device", "-fno-honor-nans",
         "-Wall", "-Wno-unused-function",
-        "-I", INCLUDE, SRC, "-o", out, *extra,
+        "-I", INCLUDE, *SRCS, "-o", out, *extra,
     ]
 
 
 def build(verbose=False):
-    """Compile the HIP source into libmi_attn.so (always recompiles)."""
+    """Compile the HIP sources into libmi_attn.so (always recompiles)."""
     tmp = LIB + ".tmp"
     cmd = compile_command(out=tmp)
     if verbose:

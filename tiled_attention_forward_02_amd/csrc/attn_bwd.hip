@@ -1,0 +1,596 @@
+// attn_bwd.hip - attention backward (dQ, dK, dV) for gfx950 (CDNA4) and its C ABI.
+//
+// The gradients of the fused attention forward ("[GPU] Deep Learning for HPC",
+// section "Flash Attention"; scale and causal flag as in the Triton forward
+// signature on null-ptr.tistory.com, category "development") for an upstream
+// gradient dO of O. The pages print no backward; it is the chain rule of the
+// forward definition: with P the softmax weights,
+//
+//   dV = P^T dO,  dP = dO V^T,  dS = P * (dP - D),  D_i = sum_c dO_ic O_ic,
+//   dQ = scale dS K,  dK = scale dS^T Q,
+//
+// where D_i equals sum_j P_ij dP_ij (the softmax Jacobian's row term) because
+// O = P V. P is never stored: it is recomputed tile by tile from the scores
+// and the forward's log-sum-exp, P = 2^(s*scale*log2(e) - lse*log2(e)).
+//
+// Two kernels on the caller's stream, no atomics, every output written once:
+//
+//  * dQ kernel: one workgroup per 128 query rows of one head (a query per
+//    lane, as in the forward), keys streamed through LDS in tiles. It also
+//    forms D_i from its own rows of O and dO and writes it to `delta`.
+//      S^T = K Q^T,  dP^T = V dO^T,  dS^T = P^T * (dP^T - D),  dQ^T += K^T dS^T
+//  * dK/dV kernel: one workgroup per 128 keys (a key per lane), query tiles
+//    streamed through LDS in row and transposed layouts.
+//      S = Q K^T,  dP = dO V^T,  dS = P * (dP - D),
+//      dV^T += dO^T P,  dK^T += Q^T dS
+//
+// In both, the C accumulator of P or dS, rounded to the input type, is the B
+// operand of the next product once the rows inside each 16-row slice follow
+// slice_pos(); the transposed LDS tiles are written in that order. Masked
+// entries (causal, and keys past Nk in the dQ kernel) get P = 0 by a select
+// after the exponent, so any finite scale works, 0 and negative included.
+// A row with lse = -inf (no visible key) gets P = 0 throughout.
+
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <type_traits>
+
+#include "common.h"
+#include "mi_attn.h"
+
+namespace {
+
+using namespace mi_attn;
+
+constexpr int kBlockRows = 32 * kWaves;  // query rows (dQ) or keys (dK/dV) per workgroup
+
+// Rows per streamed tile (keys in the dQ kernel, queries in the dK/dV
+// kernel): two rows of one 16-byte chunk per thread.
+template <int D>
+constexpr int kTileRows = D == 64 ? 64 : 32;
+
+// A tile of BR rows of a [*, D] tensor in LDS: row layout (pitch D + 8, the
+// 16-byte pad spreads the rows read by 8 lanes over distinct bank groups)
+// and transposed layout (D rows of BR, rows of each 16-row slice in
+// slice_pos order, 16-byte blocks swizzled by vt_swz).
+template <int D, int BR_>
+struct Rows {
+  static constexpr int BR = BR_;
+  static constexpr int KS = D + 8;
+  static constexpr int ROW = BR * KS;  // elements, row layout
+  static constexpr int TR = D * BR;    // elements, transposed layout
+  static constexpr int CPR = D / 8;    // 16-byte chunks per row
+  static constexpr int KPT = BR * CPR / kThreads;
+  static constexpr int VG = BR / KPT < 16 ? BR / KPT : 16;
+  static_assert(KPT == 2, "two rows per thread");
+  static_assert(BR % (VG * KPT) == 0 && VG * CPR * (BR / (VG * KPT)) == kThreads,
+                "staging covers the tile exactly once");
+};
+
+// One thread's share of staging a tile: rows kr, kr+1 of chunk dc, with the
+// row group fastest across lanes (VG lanes hold different row pairs of one
+// chunk), loaded with buffer loads (zeros past the end) and written to LDS in
+// row layout, transposed layout, or both.
+template <int D, int BR>
+struct Stager {
+  using G = Rows<D, BR>;
+  uint32_t goff;     // byte offset of row kr, chunk dc, within a tile
+  uint32_t row_wr;   // LDS byte offset, row layout
+  uint32_t t_wr[8];  // LDS byte offsets, transposed layout, per column of the chunk
+  uint32_t sel_even, sel_odd;
+
+  __device__ __forceinline__ explicit Stager(int tid) {
+    const int kr = G::KPT * (tid % G::VG) + G::VG * G::KPT * (tid / (G::VG * G::CPR));
+    const int dc = (tid / G::VG) % G::CPR;
+    goff = (uint32_t)(kr * D + 8 * dc) * 2;
+    row_wr = (uint32_t)(kr * G::KS + 8 * dc) * 2;
+    const int pos = 16 * (kr >> 4) + slice_pos(kr & 15);
+    // With 64-byte transposed rows (BR = 32), alternate lane groups write the
+    // chunk's columns in the order e ^ 1: neighbouring groups then write rows
+    // of opposite parity, on other banks.
+    const int flip = BR == 32 ? (tid / G::VG) & 1 : 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int d = 8 * dc + (e ^ flip);
+      t_wr[e] = (uint32_t)(d * BR + ((pos >> 3) ^ vt_swz<BR>(d)) * 8 + (pos & 7)) * 2;
+    }
+    // v_perm selectors for the 16-bit element at an even or odd column of a
+    // 32-bit word, swapped for the flipped lane groups.
+    sel_even = flip ? 0x07060302u : 0x05040100u;
+    sel_odd = flip ? 0x05040100u : 0x07060302u;
+  }
+  __device__ __forceinline__ void load(rsrc_t r, int row0, u32x4 (&st)[2]) const {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) st[i] = load16(r, goff + (uint32_t)((row0 + i) * D * 2));
+  }
+  __device__ __forceinline__ void store_rows(char* lds, uint32_t base,
+                                             const u32x4 (&st)[2]) const {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      *reinterpret_cast<u32x4*>(lds + base + row_wr + i * G::KS * 2) = st[i];
+  }
+  __device__ __forceinline__ void store_trans(char* lds, uint32_t base,
+                                              const u32x4 (&st)[2]) const {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t sel = (e & 1) ? sel_odd : sel_even;
+      *reinterpret_cast<uint32_t*>(lds + base + t_wr[e]) =
+          __builtin_amdgcn_perm(st[1][e >> 1], st[0][e >> 1], sel);
+    }
+  }
+};
+
+// 2^(s*c - l2), the weight of a score s given the row's lse in log2 units.
+__device__ __forceinline__ float weight(float s, float c, float l2) {
+  return __builtin_amdgcn_exp2f(fmaf(s, c, -l2));
+}
+
+// The forward's lse of a row, in log2 units; +inf for a row that sees no key
+// (lse = -inf) or lies past the end, so that its weights are all 0.
+__device__ __forceinline__ float lse_log2(float lse, bool valid) {
+  return (valid && lse != -INFINITY) ? lse * kLog2e : INFINITY;
+}
+
+// ------------------------------------------------------------- dQ kernel --
+
+template <typename E, int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(
+    const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict__ V,
+    const E* __restrict__ O, const float* __restrict__ LSE, const E* __restrict__ dO,
+    E* __restrict__ dQ, float* __restrict__ Delta, int BH, int Nq, int Nk, int nq, float c,
+    float dq_scale) {
+  constexpr int BN = kTileRows<D>;
+  using G = Rows<D, BN>;
+  constexpr int KS = G::KS, NKB = BN / 32;
+  // Stage: K rows | V rows | K^T.
+  constexpr int V_OFF = G::ROW * 2, KT_OFF = 2 * G::ROW * 2;
+  constexpr int STAGE = (2 * G::ROW + G::TR) * 2;
+  typedef typename Elem<E>::v8 v8;
+  typedef typename Elem<E>::v4 v4;
+  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, col = lane & 31, half = lane >> 5;
+  int bh, qt;
+  map_block(blockIdx.x, BH, nq, CAUSAL, bh, qt);
+  const int q0 = qt * kBlockRows;
+  const int qw = q0 + 32 * wave;
+  const int qi = qw + col;
+  const int off = Nk - Nq;  // query i sits at key position i + off
+
+  const size_t qhead = (size_t)bh * (size_t)Nq * D;
+  const size_t khead = (size_t)bh * (size_t)Nk * D;
+  const uint32_t q_bytes = (uint32_t)Nq * D * 2;
+  const uint32_t k_bytes = (uint32_t)Nk * D * 2;
+  const rsrc_t rk = make_rsrc(K + khead, k_bytes);
+  const rsrc_t rv = make_rsrc(V + khead, k_bytes);
+
+  // Q^T and dO^T fragments (B operands, a query per lane), and D_i from this
+  // lane's half of the row of dO * O, both halves combined.
+  v8 qf[D / 16], df[D / 16];
+  float dpart = 0.f;
+  {
+    const rsrc_t rq = make_rsrc(Q + qhead, q_bytes);
+    const rsrc_t rdo = make_rsrc(dO + qhead, q_bytes);
+    const rsrc_t ro = make_rsrc(O + qhead, q_bytes);
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      const uint32_t at = (uint32_t)(qi * D + 16 * s + 8 * half) * 2;
+      qf[s] = __builtin_bit_cast(v8, load16(rq, at));
+      df[s] = __builtin_bit_cast(v8, load16(rdo, at));
+      const v8 o8 = __builtin_bit_cast(v8, load16(ro, at));
+#pragma unroll
+      for (int j = 0; j < 8; ++j) dpart = fmaf((float)df[s][j], (float)o8[j], dpart);
+    }
+  }
+  const float delta = swap_halves_add(dpart);
+  const rsrc_t rl = make_rsrc(LSE + (size_t)bh * Nq, (uint32_t)Nq * 4);
+  const float l2 = lse_log2(
+      __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rl, qi * 4, 0, 0)), qi < Nq);
+  if (half == 0) {
+    const rsrc_t rd = make_rsrc(Delta + (size_t)bh * Nq, (uint32_t)Nq * 4);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(delta), rd, qi * 4, 0, 0);
+  }
+
+  const int kv_end = CAUSAL ? min(Nk, q0 + kBlockRows + off) : Nk;
+  const int nt = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
+  const int wave_kv_end = CAUSAL ? min(Nk, qw + 32 + off) : Nk;
+
+  const Stager<D, BN> stg(tid);
+  u32x4 kst[2], vst[2];
+  auto gload = [&](int k0) __attribute__((always_inline)) {
+    stg.load(rk, k0, kst);
+    stg.load(rv, k0, vst);
+  };
+  char* const lds = smem;
+  auto lds_store = [&](auto stage_c) __attribute__((always_inline)) {
+    constexpr uint32_t base = decltype(stage_c)::value * STAGE;
+    stg.store_rows(lds, base, kst);
+    stg.store_rows(lds, base + V_OFF, vst);
+    stg.store_trans(lds, base + KT_OFF, kst);
+  };
+  const uint32_t r_rd = (uint32_t)(col * KS + 8 * half) * 2;
+  uint32_t t_rd[BN / 16];
+#pragma unroll
+  for (int g = 0; g < BN / 16; ++g)
+    t_rd[g] = KT_OFF + (uint32_t)(col * BN + ((2 * g + half) ^ vt_swz<BN>(col)) * 8) * 2;
+
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
+
+  auto step = [&](int t, auto stage_c) __attribute__((always_inline)) {
+    constexpr uint32_t base = decltype(stage_c)::value * STAGE;
+    const int k0 = t * BN;
+    const bool has_next = t + 1 < nt;
+    if (has_next) gload(k0 + BN);
+
+    if (k0 < wave_kv_end) {
+      // S^T = K Q^T and dP^T = V dO^T, 32 keys per accumulator.
+      f32x16 sacc[NKB], pacc[NKB];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        sacc[kb] = f32x16{};
+        pacc[kb] = f32x16{};
+#pragma unroll
+        for (int j = 0; j < D / 16; ++j) {
+          const uint32_t at = base + r_rd + (32 * kb * KS + 16 * j) * 2;
+          sacc[kb] = Elem<E>::mfma(*reinterpret_cast<const v8*>(lds + at), qf[j], sacc[kb]);
+          pacc[kb] = Elem<E>::mfma(*reinterpret_cast<const v8*>(lds + at + V_OFF), df[j],
+                                   pacc[kb]);
+        }
+      }
+      // P, with 0 for keys past Nk and (causal) keys after the query.
+      float p[NKB][16];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) p[kb][i] = weight(sacc[kb][i], c, l2);
+      if ((k0 + BN > Nk) || (CAUSAL && k0 + BN - 1 > qw + off)) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = k0 + 32 * kb + 8 * (i >> 2) + 4 * half + (i & 3);
+            if (key >= Nk || (CAUSAL && key > qi + off)) p[kb][i] = 0.f;
+          }
+      }
+      // dS^T = P^T (dP^T - D), rounded: the B operand of dQ^T += K^T dS^T.
+      v8 dsb[NKB][2];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) dsb[kb][i >> 3][i & 7] = (E)(p[kb][i] * (pacc[kb][i] - delta));
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int sg = 0; sg < 2; ++sg)
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db) {
+            const v8 a = *reinterpret_cast<const v8*>(lds + base + t_rd[2 * kb + sg] +
+                                                      32 * db * BN * 2);
+            acc[db] = Elem<E>::mfma(a, dsb[kb][sg], acc[db]);
+          }
+    }
+
+    if (has_next) lds_store(std::integral_constant<int, decltype(stage_c)::value ^ 1>{});
+    __syncthreads();
+  };
+
+  if (nt > 0) {
+    gload(0);
+    lds_store(std::integral_constant<int, 0>{});
+    __syncthreads();
+  }
+  for (int t = 0; t < nt; t += 2) {
+    step(t, std::integral_constant<int, 0>{});
+    if (t + 1 < nt) step(t + 1, std::integral_constant<int, 1>{});
+  }
+
+  // dQ = scale * acc; rows past Nq are dropped by the range check.
+  const rsrc_t rdq = make_rsrc(dQ + qhead, q_bytes);
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      v4 o4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o4[e] = (E)(acc[db][4 * r + e] * dq_scale);
+      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, o4), rdq,
+                                            (int)((qi * D + 32 * db + 8 * r + 4 * half) * 2),
+                                            0, 0);
+    }
+}
+
+// ---------------------------------------------------------- dK/dV kernel --
+
+template <typename E, int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, D >= 128 ? 1 : 2) void attn_bwd_dkdv_kernel(
+    const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict__ V,
+    const float* __restrict__ LSE, const E* __restrict__ dO, const float* __restrict__ Delta,
+    E* __restrict__ dK, E* __restrict__ dV, int BH, int Nq, int Nk, int nk, float c,
+    float dk_scale) {
+  constexpr int BQ = kTileRows<D>;
+  using G = Rows<D, BQ>;
+  constexpr int KS = G::KS, NQB = BQ / 32;
+  // Stage: Q rows | dO rows | Q^T | dO^T | lse (log2) [BQ] | D [BQ].
+  constexpr int DO_OFF = G::ROW * 2;
+  constexpr int QT_OFF = 2 * G::ROW * 2;
+  constexpr int DOT_OFF = QT_OFF + G::TR * 2;
+  constexpr int L_OFF = DOT_OFF + G::TR * 2;
+  constexpr int D_OFF = L_OFF + BQ * 4;
+  constexpr int STAGE = D_OFF + BQ * 4;
+  typedef typename Elem<E>::v8 v8;
+  typedef typename Elem<E>::v4 v4;
+  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, col = lane & 31, half = lane >> 5;
+  int bh, kt;
+  map_block(blockIdx.x, BH, nk, CAUSAL, bh, kt);
+  // Causal: key tile 0 sees the most queries; map_block deals the last index
+  // first, so number the key tiles from the end.
+  if (CAUSAL) kt = nk - 1 - kt;
+  const int k0 = kt * kBlockRows;
+  const int kw = k0 + 32 * wave;  // first key of this wave
+  const int kj = kw + col;        // this lane's key
+  const int off = Nk - Nq;        // query i sees key j iff j <= i + off (causal)
+
+  const size_t qhead = (size_t)bh * (size_t)Nq * D;
+  const size_t khead = (size_t)bh * (size_t)Nk * D;
+  const uint32_t q_bytes = (uint32_t)Nq * D * 2;
+  const uint32_t k_bytes = (uint32_t)Nk * D * 2;
+  const rsrc_t rq = make_rsrc(Q + qhead, q_bytes);
+  const rsrc_t rdo = make_rsrc(dO + qhead, q_bytes);
+  const rsrc_t rl = make_rsrc(LSE + (size_t)bh * Nq, (uint32_t)Nq * 4);
+  const rsrc_t rd = make_rsrc(Delta + (size_t)bh * Nq, (uint32_t)Nq * 4);
+
+  // K^T and V^T fragments (B operands, a key per lane); zero past Nk.
+  v8 kf[D / 16], vf[D / 16];
+  {
+    const rsrc_t rk = make_rsrc(K + khead, k_bytes);
+    const rsrc_t rv = make_rsrc(V + khead, k_bytes);
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      const uint32_t at = (uint32_t)(kj * D + 16 * s + 8 * half) * 2;
+      kf[s] = __builtin_bit_cast(v8, load16(rk, at));
+      vf[s] = __builtin_bit_cast(v8, load16(rv, at));
+    }
+  }
+
+  // Query tiles that can see a key of this workgroup: i >= k0 - off.
+  const int q_begin = CAUSAL ? max(0, k0 - off) : 0;
+  const int qt0 = q_begin / BQ;
+  const int nt = q_begin < Nq ? (Nq + BQ - 1) / BQ - qt0 : 0;
+
+  const Stager<D, BQ> stg(tid);
+  u32x4 qst[2], dst[2];
+  float lst = 0.f, dlt = 0.f;
+  auto gload = [&](int q0) __attribute__((always_inline)) {
+    stg.load(rq, q0, qst);
+    stg.load(rdo, q0, dst);
+    if (tid < BQ) {
+      const int qrow = q0 + tid;
+      lst = lse_log2(__uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rl, qrow * 4, 0, 0)),
+                     qrow < Nq);
+      dlt = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rd, qrow * 4, 0, 0));
+    }
+  };
+  char* const lds = smem;
+  auto lds_store = [&](auto stage_c) __attribute__((always_inline)) {
+    constexpr uint32_t base = decltype(stage_c)::value * STAGE;
+    stg.store_rows(lds, base, qst);
+    stg.store_rows(lds, base + DO_OFF, dst);
+    stg.store_trans(lds, base + QT_OFF, qst);
+    stg.store_trans(lds, base + DOT_OFF, dst);
+    if (tid < BQ) {
+      *reinterpret_cast<float*>(lds + base + L_OFF + tid * 4) = lst;
+      *reinterpret_cast<float*>(lds + base + D_OFF + tid * 4) = dlt;
+    }
+  };
+  const uint32_t r_rd = (uint32_t)(col * KS + 8 * half) * 2;
+  uint32_t t_rd[BQ / 16];
+#pragma unroll
+  for (int g = 0; g < BQ / 16; ++g)
+    t_rd[g] = (uint32_t)(col * BQ + ((2 * g + half) ^ vt_swz<BQ>(col)) * 8) * 2;
+
+  f32x16 dkacc[D / 32], dvacc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+    dkacc[db] = f32x16{};
+    dvacc[db] = f32x16{};
+  }
+
+  auto step = [&](int t, auto stage_c) __attribute__((always_inline)) {
+    constexpr uint32_t base = decltype(stage_c)::value * STAGE;
+    const int q0 = (qt0 + t) * BQ;
+    const bool has_next = t + 1 < nt;
+    if (has_next) gload(q0 + BQ);
+
+    // Some query of the tile sees a key of this wave.
+    if (!CAUSAL || q0 + BQ - 1 + off >= kw) {
+      // S = Q K^T and dP = dO V^T, 32 queries per accumulator.
+      f32x16 sacc[NQB], pacc[NQB];
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+        sacc[qb] = f32x16{};
+        pacc[qb] = f32x16{};
+#pragma unroll
+        for (int j = 0; j < D / 16; ++j) {
+          const uint32_t at = base + r_rd + (32 * qb * KS + 16 * j) * 2;
+          sacc[qb] = Elem<E>::mfma(*reinterpret_cast<const v8*>(lds + at), kf[j], sacc[qb]);
+          pacc[qb] = Elem<E>::mfma(*reinterpret_cast<const v8*>(lds + at + DO_OFF), vf[j],
+                                   pacc[qb]);
+        }
+      }
+      // Register i of block qb holds query q0 + 32qb + 8(i/4) + 4h + i%4: its
+      // lse and D come four at a time from LDS.
+      const bool masked = CAUSAL && q0 + off < kw + 31;
+      v8 pb[NQB][2], dsb[NQB][2];
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = 32 * qb + 8 * r + 4 * half;
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(lds + base + L_OFF + row * 4);
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(lds + base + D_OFF + row * 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int i = 4 * r + e;
+            float p = weight(sacc[qb][i], c, l4[e]);
+            if (masked && kj > q0 + row + e + off) p = 0.f;
+            pb[qb][i >> 3][i & 7] = (E)p;
+            dsb[qb][i >> 3][i & 7] = (E)(p * (pacc[qb][i] - d4[e]));
+          }
+        }
+      // dV^T += dO^T P and dK^T += Q^T dS, 16 queries per MFMA.
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+        for (int sg = 0; sg < 2; ++sg)
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db) {
+            const uint32_t at = base + t_rd[2 * qb + sg] + 32 * db * BQ * 2;
+            dvacc[db] = Elem<E>::mfma(*reinterpret_cast<const v8*>(lds + at + DOT_OFF),
+                                      pb[qb][sg], dvacc[db]);
+            dkacc[db] = Elem<E>::mfma(*reinterpret_cast<const v8*>(lds + at + QT_OFF),
+                                      dsb[qb][sg], dkacc[db]);
+          }
+    }
+
+    if (has_next) lds_store(std::integral_constant<int, decltype(stage_c)::value ^ 1>{});
+    __syncthreads();
+  };
+
+  if (nt > 0) {
+    gload(qt0 * BQ);
+    lds_store(std::integral_constant<int, 0>{});
+    __syncthreads();
+  }
+  for (int t = 0; t < nt; t += 2) {
+    step(t, std::integral_constant<int, 0>{});
+    if (t + 1 < nt) step(t + 1, std::integral_constant<int, 1>{});
+  }
+
+  // dK = scale * dK^T acc, dV = dV^T acc; keys past Nk are dropped.
+  const rsrc_t rdk = make_rsrc(dK + khead, k_bytes);
+  const rsrc_t rdv = make_rsrc(dV + khead, k_bytes);
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      v4 k4, v4_;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        k4[e] = (E)(dkacc[db][4 * r + e] * dk_scale);
+        v4_[e] = (E)dvacc[db][4 * r + e];
+      }
+      const int at = (kj * D + 32 * db + 8 * r + 4 * half) * 2;
+      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, k4), rdk, at, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v4_), rdv, at, 0, 0);
+    }
+}
+
+// ------------------------------------------------------------- host side --
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || !na || !nb) return false;
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+struct BwdArgs {
+  const void *q, *k, *v, *o, *d_o;
+  const float* lse;
+  void *dq, *dk, *dv;
+  float* delta;
+  int BH, Nq, Nk, nq, nk;
+  float c, scale;
+  hipStream_t stream;
+};
+
+template <typename E, int D, bool CAUSAL>
+hipError_t launch_bwd(const BwdArgs& a) {
+  const E* q = static_cast<const E*>(a.q);
+  const E* k = static_cast<const E*>(a.k);
+  const E* v = static_cast<const E*>(a.v);
+  const E* o = static_cast<const E*>(a.o);
+  const E* d_o = static_cast<const E*>(a.d_o);
+  E* dq = static_cast<E*>(a.dq);
+  E* dk = static_cast<E*>(a.dk);
+  E* dv = static_cast<E*>(a.dv);
+  const float* lse = a.lse;
+  float* delta = a.delta;
+  int BH = a.BH, Nq = a.Nq, Nk = a.Nk, nq = a.nq, nk = a.nk;
+  float c = a.c, scale = a.scale;
+  // dQ (and D) first: the dK/dV kernel reads D.
+  if (nq > 0) {
+    void* args[] = {&q, &k, &v, &o, &lse, &d_o, &dq, &delta, &BH, &Nq, &Nk, &nq, &c, &scale};
+    const hipError_t err =
+        hipLaunchKernel(reinterpret_cast<const void*>(&attn_bwd_dq_kernel<E, D, CAUSAL>),
+                        dim3(BH * nq), dim3(kThreads), args, 0, a.stream);
+    if (err != hipSuccess) return err;
+  }
+  if (nk > 0) {
+    void* args[] = {&q, &k, &v, &lse, &d_o, &delta, &dk, &dv, &BH, &Nq, &Nk, &nk, &c, &scale};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&attn_bwd_dkdv_kernel<E, D, CAUSAL>),
+                           dim3(BH * nk), dim3(kThreads), args, 0, a.stream);
+  }
+  return hipSuccess;
+}
+
+template <typename E>
+hipError_t launch_bwd_type(const BwdArgs& a, int d, bool causal) {
+  if (d == 64) return causal ? launch_bwd<E, 64, true>(a) : launch_bwd<E, 64, false>(a);
+  return causal ? launch_bwd<E, 128, true>(a) : launch_bwd<E, 128, false>(a);
+}
+
+}  // namespace
+
+extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                        const float* lse, const void* d_o, void* dq, void* dk, void* dv,
+                        float* delta, int B, int H, int Nq, int Nk, int d, int dtype,
+                        float scale, int causal, void* stream) {
+  if (B < 0 || H < 0 || Nq < 0 || Nk < 0) return ATTN_ERR_SHAPE;
+  if (d != 64 && d != 128) return ATTN_ERR_HEADDIM;
+  if ((int64_t)Nq * d * 2 + (int64_t)kBlockRows * d * 2 > INT32_MAX) return ATTN_ERR_SHAPE;
+  if ((int64_t)Nk * d * 2 + (int64_t)kBlockRows * d * 2 > INT32_MAX) return ATTN_ERR_SHAPE;
+  const int64_t BH = (int64_t)B * H;
+  const int64_t nq = ((int64_t)Nq + kBlockRows - 1) / kBlockRows;
+  const int64_t nk = ((int64_t)Nk + kBlockRows - 1) / kBlockRows;
+  if (BH * nq > INT32_MAX || BH * nk > INT32_MAX) return ATTN_ERR_SHAPE;
+  if (dtype != ATTN_BF16 && dtype != ATTN_F16) return ATTN_ERR_DTYPE;
+  uint32_t sbits;
+  memcpy(&sbits, &scale, 4);
+  if ((sbits & 0x7f800000u) == 0x7f800000u) return ATTN_ERR_SCALE;
+  if (BH == 0 || (Nq == 0 && Nk == 0)) return ATTN_OK;
+  if (Nq > 0 && (!q || !o || !lse || !d_o || !dq || !delta)) return ATTN_ERR_NULL;
+  if (Nk > 0 && (!k || !v || !dk || !dv)) return ATTN_ERR_NULL;
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)d_o |
+       (uintptr_t)dq | (uintptr_t)dk | (uintptr_t)dv) & 15)
+    return ATTN_ERR_ALIGN;
+  if (((uintptr_t)lse | (uintptr_t)delta) & 3) return ATTN_ERR_ALIGN;
+  const size_t qb = (size_t)BH * Nq * d * 2, kb = (size_t)BH * Nk * d * 2;
+  const size_t lb = (size_t)BH * Nq * 4;
+  const struct {
+    const void* p;
+    size_t n;
+  } in[] = {{q, qb}, {k, kb}, {v, kb}, {o, qb}, {lse, lb}, {d_o, qb}},
+    out[] = {{dq, qb}, {dk, kb}, {dv, kb}, {delta, lb}};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 6; ++j)
+      if (overlaps(out[i].p, out[i].n, in[j].p, in[j].n)) return ATTN_ERR_ALIAS;
+    for (int j = 0; j < i; ++j)
+      if (overlaps(out[i].p, out[i].n, out[j].p, out[j].n)) return ATTN_ERR_ALIAS;
+  }
+
+  const BwdArgs a{q, k, v, o, d_o, lse, dq, dk, dv, delta, (int)BH, Nq, Nk, (int)nq, (int)nk,
+                  scale * kLog2e, scale, static_cast<hipStream_t>(stream)};
+  const hipError_t err = dtype == ATTN_BF16 ? launch_bwd_type<__bf16>(a, d, causal != 0)
+                                            : launch_bwd_type<_Float16>(a, d, causal != 0);
+  return err == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}

@@ -1,0 +1,125 @@
+// common.h - device helpers shared by the attention forward and backward
+// kernels for gfx950 (CDNA4): element types and their MFMA, buffer resources,
+// lane-half exchange, the key order inside a 16-key slice, the V^T / Q^T LDS
+// swizzle and the workgroup -> tile mapping.
+//
+// MFMA 32x32x16 fragment layout used throughout (lane l, h = l / 32, c = l % 32):
+//   A (32 x 16):  lane holds row c, k-elements 8h .. 8h+7
+//   B (16 x 32):  lane holds column c, k-elements 8h .. 8h+7
+//   C (32 x 32):  register i holds row 8*(i/4) + 4h + i%4, column c
+// A and B agree on which k each (h, element) carries, so any hardware k order
+// gives the same contraction.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+namespace mi_attn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// The two 16-bit input types: 8-element MFMA operands, the 32x32x16 MFMA
+// with fp32 accumulation, and rounding from fp32 (to nearest even).
+template <typename E>
+struct Elem;
+template <>
+struct Elem<__bf16> {
+  typedef bf16x8 v8;
+  typedef bf16x4 v4;
+  static __device__ __forceinline__ f32x16 mfma(v8 a, v8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+};
+template <>
+struct Elem<_Float16> {
+  typedef f16x8 v8;
+  typedef f16x4 v4;
+  static __device__ __forceinline__ f32x16 mfma(v8 a, v8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+};
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+constexpr int kWaves = 4;              // waves per workgroup
+constexpr int kThreads = 64 * kWaves;  // threads per workgroup
+
+// Key order inside a 16-key slice of a transposed tile in LDS: swaps bits 2
+// and 3 of the offset, matching where a C accumulator leaves each row (C
+// layout row 8*(i/4) + 4h + i%4 read as B-operand element 8h + j). Its own
+// inverse.
+__device__ __forceinline__ int slice_pos(int o) {
+  return (o & 3) | ((o & 4) << 1) | ((o & 8) >> 1);
+}
+
+// XOR swizzle of the 16-byte blocks of a transposed tile's row (BN/8 blocks),
+// a function of the row index mod 32 only (the same for every 32-row block a
+// lane reads): any 8 aligned consecutive rows, and any 16, land on distinct
+// bank groups, whether a row is 128 bytes (BN = 64) or 64 bytes (BN = 32).
+template <int BN>
+__device__ __forceinline__ int vt_swz(int d) {
+  d &= 31;
+  return BN >= 64 ? ((d ^ (d >> 3)) & 7) : (((d >> 1) ^ (d >> 3)) & 3);
+}
+
+// Workgroup id -> (batch*head, tile). Workgroups are dealt to the 8 XCDs
+// round-robin, so when B*H is a multiple of 8 each XCD gets the heads
+// h = x (mod 8) and walks them head by head (not heaviest_first: the tiles of
+// one head run together and share that XCD's L2) or tile by tile from the
+// last index down (heaviest_first: the caller numbers tiles so that the last
+// is the heaviest; short tiles fill the tail).
+__device__ __forceinline__ void map_block(int bid, int BH, int nt, bool heaviest_first,
+                                          int& bh, int& t) {
+  if ((BH & 7) == 0) {
+    const int x = bid & 7, j = bid >> 3, hpx = BH >> 3;
+    if (heaviest_first) {
+      t = nt - 1 - j / hpx;
+      bh = x + 8 * (j % hpx);
+    } else {
+      bh = x + 8 * (j / nt);
+      t = j % nt;
+    }
+  } else if (heaviest_first) {
+    t = nt - 1 - bid / BH;
+    bh = bid % BH;
+  } else {
+    bh = bid / nt;
+    t = bid % nt;
+  }
+}
+
+// Buffer resource over [base, base + bytes): loads past the end return 0 and
+// stores past the end are dropped by the hardware range check.
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+__device__ __forceinline__ u32x4 load16(rsrc_t r, uint32_t byte_off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 0);
+}
+
+// Value of x in the lane 32 positions away, combined with op (same result in
+// both lanes of the pair, bit for bit).
+__device__ __forceinline__ float swap_halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float swap_halves_add(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+}  // namespace mi_attn
