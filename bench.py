@@ -50,9 +50,11 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2516.6
 HBM_PEAK_GBS = 8000.0
 DEFAULT_WORKLOAD = "b16h16n4096d128"
-CSRC = os.path.join(ROOT, "tiled_attention_forward_02_amd", "csrc")
-# The sources each timed pass is built from (hashed to tie profiles to code).
-KERNEL_SRCS = {"fwd": ("attn_fwd.hip", "common.h"), "bwd": ("attn_bwd.hip", "common.h")}
+PKG = os.path.join(ROOT, "tiled_attention_forward_02_amd")
+# The files each timed pass is built from, its compile flags included (hashed
+# to tie profiles to code).
+KERNEL_SRCS = {"fwd": ("csrc/attn_fwd.hip", "csrc/common.h", "build.py"),
+               "bwd": ("csrc/attn_bwd.hip", "csrc/common.h", "build.py")}
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -63,7 +65,7 @@ def log(*a):
 def kernel_sha(which="fwd"):
     h = hashlib.sha256()
     for name in KERNEL_SRCS[which]:
-        with open(os.path.join(CSRC, name), "rb") as f:
+        with open(os.path.join(PKG, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 

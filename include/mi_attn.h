@@ -131,8 +131,8 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse
  *             A row with lse = -inf (it saw no key) has p = 0.
  *   d_o       upstream gradient [B, H, Nq, d].
  *   dq        [B, H, Nq, d]; dk, dv [B, H, Nk, d]; written, every element.
- *   delta     float32 [B, H, Nq], caller-owned; receives D_i (it is read back
- *             by the second of the two kernels the call queues).
+ *   delta     float32 [B, H, Nq], caller-owned; receives D_i (the first kernel
+ *             the call queues writes it, a later one reads it back).
  *   B, H, Nq, Nk, d, dtype, scale, causal, stream: as for attn_fwd_ex, except
  *             that d must be 64 or 128.
  *

@@ -10,10 +10,20 @@ import os
 import shutil
 import subprocess
 import sys
+import tempfile
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG_DIR)
-SRCS = [os.path.join(PKG_DIR, "csrc", f) for f in ("attn_fwd.hip", "attn_bwd.hip")]
+CSRC = os.path.join(PKG_DIR, "csrc")
+# Each source with its own extra device flags. The backward's dK/dV kernel
+# keeps two fp32 accumulators and the K, V fragments live; left to its
+# heuristics the compiler gives its MFMAs accumulators in AGPRs and copies
+# them to VGPRs and back on every loop iteration, so the VGPR form is forced
+# there (the forward is unaffected: it is compiled on its own).
+SOURCES = (
+    ("attn_fwd.hip", ()),
+    ("attn_bwd.hip", ("-mllvm", "-amdgpu-mfma-vgpr-form=1")),
+)
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG_DIR, "libmi_attn.so")
 ARCH = "gfx950"
@@ -26,22 +36,18 @@ def hipcc():
     raise RuntimeError("hipcc not found (ROCm is required to build libmi_attn)")
 
 
-def compile_command(out=LIB, extra=()):
-    return [
-        hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-        # packed fp32 VALU forms are kept off: plain fp32 code only
-        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-        # NaN-free max/min on the device side only (no canonicalising moves)
-        "-Xarch_device", "-fno-honor-nans",
-        "-Wall", "-Wno-unused-function",
-        "-I", INCLUDE, *SRCS, "-o", out, *extra,
-    ]
+COMMON = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+    # packed fp32 VALU forms are kept off: plain fp32 code only
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # NaN-free max/min on the device side only (no canonicalising moves)
+    "-Xarch_device", "-fno-honor-nans",
+    "-Wall", "-Wno-unused-function",
+    "-I", INCLUDE,
+]
 
 
-def build(verbose=False):
-    """Compile the HIP sources into libmi_attn.so (always recompiles)."""
-    tmp = LIB + ".tmp"
-    cmd = compile_command(out=tmp)
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -52,6 +58,18 @@ def build(verbose=False):
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
     if verbose and err.strip():
         print(err, file=sys.stderr)
+
+
+def build(verbose=False):
+    """Compile the HIP sources into libmi_attn.so (always recompiles)."""
+    with tempfile.TemporaryDirectory(prefix="mi_attn_build_") as tmpdir:
+        objs = []
+        for name, extra in SOURCES:
+            obj = os.path.join(tmpdir, name + ".o")
+            _run([hipcc(), *COMMON, *extra, "-c", os.path.join(CSRC, name), "-o", obj], verbose)
+            objs.append(obj)
+        tmp = LIB + ".tmp"
+        _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)
     return LIB
 
