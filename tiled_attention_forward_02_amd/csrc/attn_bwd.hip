@@ -393,16 +393,19 @@ __global__ __launch_bounds__(kThreads, P == kDV ? 3 : 2) void attn_bwd_kv_kernel
 
   const Stager<D, BQ> stg(tid);
   u32x4 qst[2], dst[2];
-  float lst = 0.f, dlt = 0.f;
+  // lse and D of the next tile's rows (threads tid < BQ), kept raw until the
+  // tile is written to LDS: using them at once would wait for every load in
+  // flight, the tile's own included.
+  uint32_t lraw = 0, draw = 0;
+  bool lvalid = false;
   auto gload = [&](int q0) __attribute__((always_inline)) {
     stg.load(rq, q0, qst);
     stg.load(rdo, q0, dst);
     if (tid < BQ) {
       const int qrow = q0 + tid;
-      lst = lse_log2(__uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rl, qrow * 4, 0, 0)),
-                     qrow < Nq);
-      if constexpr (S_::kDelta)
-        dlt = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rd, qrow * 4, 0, 0));
+      lvalid = qrow < Nq;
+      lraw = __builtin_amdgcn_raw_buffer_load_b32(rl, qrow * 4, 0, 0);
+      if constexpr (S_::kDelta) draw = __builtin_amdgcn_raw_buffer_load_b32(rd, qrow * 4, 0, 0);
     }
   };
   char* const lds = smem;
@@ -413,8 +416,9 @@ __global__ __launch_bounds__(kThreads, P == kDV ? 3 : 2) void attn_bwd_kv_kernel
     if constexpr (S_::kQT) stg.store_trans(lds, base + S_::QT_OFF, qst);
     if constexpr (S_::kDOT) stg.store_trans(lds, base + S_::DOT_OFF, dst);
     if (tid < BQ) {
-      *reinterpret_cast<float*>(lds + base + S_::L_OFF + tid * 4) = lst;
-      if constexpr (S_::kDelta) *reinterpret_cast<float*>(lds + base + S_::D_OFF + tid * 4) = dlt;
+      *reinterpret_cast<float*>(lds + base + S_::L_OFF + tid * 4) =
+          lse_log2(__uint_as_float(lraw), lvalid);
+      if constexpr (S_::kDelta) *reinterpret_cast<uint32_t*>(lds + base + S_::D_OFF + tid * 4) = draw;
     }
   };
   const uint32_t r_rd = (uint32_t)(col * KS + 8 * half) * 2;
