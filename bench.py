@@ -8,7 +8,7 @@ A step is one attn_fwd call over the whole workload (every query row of every
 (batch, head)) with inputs already resident in HBM. The default workload is
 the non-causal d=128, N=4096 one (B=16, H=16) that the throughput target is
 quoted on. --head-dim and --dtype keep the workload's B, H, N and causality
-and change the head dimension (32, 64, 128, 256) or the element type (float16
+and change the head dimension (32, 64, 96, 128, 256) or the element type (float16
 goes through attn_fwd_ex); the workload name then carries the change. Prints
 ONE JSON line on stdout; diagnostics go to stderr.
 
@@ -184,7 +184,7 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--head-dim", type=int, default=0, choices=[0, 32, 64, 128, 256])
+    ap.add_argument("--head-dim", type=int, default=0, choices=[0, 32, 64, 96, 128, 256])
     ap.add_argument("--dtype", default="bf16", choices=["bf16", "f16"])
     ap.add_argument("--pass", dest="which", default="fwd", choices=["fwd", "bwd"])
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -31,7 +31,7 @@ typedef enum {
   ATTN_OK = 0,
   ATTN_ERR_NULL = -1,      /* a required pointer (q, k, v, o, lse, or an out-param) is NULL */
   ATTN_ERR_SHAPE = -2,     /* a size is negative, or one head (N*d*2 bytes) reaches 2^31 */
-  ATTN_ERR_HEADDIM = -3,   /* d is not one of 32, 64, 128, 256 (attn_bwd: 64, 128) */
+  ATTN_ERR_HEADDIM = -3,   /* d is not one of 32, 64, 96, 128, 256 (attn_bwd: 64, 128) */
   ATTN_ERR_ALIGN = -5,     /* q, k, v or o not 16-byte aligned, or lse not 4-byte aligned */
   ATTN_ERR_ALIAS = -6,     /* o or lse overlaps an input, or o overlaps lse */
   ATTN_ERR_SCALE = -7,     /* scale is NaN or infinite */
@@ -55,7 +55,7 @@ typedef enum {
  *   B, H, N  batch size, heads, sequence length (queries and keys share N).
  *            Any N >= 1 is accepted (no multiple-of-tile restriction). If
  *            B*H*N == 0 the call does nothing and returns ATTN_OK.
- *   d        head dimension: 32, 64, 128 or 256.
+ *   d        head dimension: 32, 64, 96, 128 or 256.
  *   scale    softmax scale, applied to Q K^T before masking; used exactly as
  *            the given float32 value. Any finite value (0 and negative
  *            included) is accepted.

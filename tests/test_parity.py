@@ -327,7 +327,7 @@ EX_SELF = [(1, 1, 1), (1, 2, 17), (2, 3, 100), (1, 1, 129), (2, 2, 300), (1, 3, 
 
 
 @pytest.mark.parametrize("dt", ["bf16", "f16"])
-@pytest.mark.parametrize("d", [32, 64, 128, 256])
+@pytest.mark.parametrize("d", [32, 64, 96, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("B,H,N", EX_SELF)
 def test_ex_self(B, H, N, d, causal, dt):
@@ -344,7 +344,7 @@ EX_CROSS = [(1, 1), (3, 2), (100, 37), (37, 100), (129, 1000), (1000, 129), (200
 
 
 @pytest.mark.parametrize("dt", ["bf16", "f16"])
-@pytest.mark.parametrize("d", [32, 256])
+@pytest.mark.parametrize("d", [32, 96, 256])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("Nq,Nk", EX_CROSS)
 def test_ex_cross(Nq, Nk, d, causal, dt):
@@ -357,7 +357,7 @@ def test_ex_cross(Nq, Nk, d, causal, dt):
     check_with_empty_rows(o, lse, o_ref, lse_ref, f"cross {Nq}x{Nk} d={d} {dt}")
 
 
-@pytest.mark.parametrize("d", [32, 256])
+@pytest.mark.parametrize("d", [32, 96, 256])
 @pytest.mark.parametrize("dt", ["bf16", "f16"])
 def test_ex_without_keys(d, dt):
     announce(f"ex Nk=0 d={d} {dt}")
@@ -384,7 +384,7 @@ def test_ex_bf16_is_attn_fwd_cross():
 
 
 @pytest.mark.parametrize("dt", ["bf16", "f16"])
-@pytest.mark.parametrize("d", [32, 256])
+@pytest.mark.parametrize("d", [32, 96, 256])
 def test_ex_zero_query_gives_mean_of_visible_values(d, dt):
     """q = 0: every visible key has weight 1/count, so O is a running mean of
     V and lse = ln(count), at any size."""
@@ -402,10 +402,10 @@ def test_ex_zero_query_gives_mean_of_visible_values(d, dt):
 
 
 @pytest.mark.parametrize("dt", ["bf16", "f16"])
-@pytest.mark.parametrize("d,N,causal", [(32, 16384, True), (256, 8192, False),
-                                        (256, 8192, True)])
+@pytest.mark.parametrize("d,N,causal", [(32, 16384, True), (96, 16384, True),
+                                        (256, 8192, False), (256, 8192, True)])
 def test_ex_long_sampled(d, N, causal, dt):
-    """Long sequences at the new head dims: 48 sampled rows per head (the first,
+    """Long sequences at the other head dims: 48 sampled rows per head (the first,
     the last, and rows around tile edges) against the oracle row by row."""
     announce(f"ex long d={d} N={N} causal={causal} {dt}")
     inp = make_inputs(WORKLOADS[4], B=1, H=4, N=N, d=d, seed=7000 + d, dtype=DTYPES[dt])

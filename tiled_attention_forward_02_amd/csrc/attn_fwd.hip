@@ -60,7 +60,7 @@ constexpr float kLazySum = 4096.f;  // largest per-lane tile sum kept on a stale
 // where the 32-key tile's scores are cheap to keep live) or row maximum
 // first (d=64, where keeping 64 scores live would cost a wave per SIMD).
 template <int D>
-constexpr bool kSpeculativeWeights = D >= 128;
+constexpr bool kSpeculativeWeights = D >= 96;
 
 constexpr int kBlockM = 32 * kWaves;   // query rows per workgroup
 // Keys per tile for head dimension D. At d=128 a 32-key tile keeps a wave
@@ -71,9 +71,17 @@ constexpr int kBlockN = 64;
 template <>
 constexpr int kBlockN<32> = 128;  // each thread still stages 2 keys of 8 columns
 template <>
+constexpr int kBlockN<96> = 32;
+template <>
 constexpr int kBlockN<128> = 32;
 template <>
 constexpr int kBlockN<256> = 32;
+
+// Head dimension of the LDS tile layout: d = 96 tiles are laid out as d = 128
+// ones (12 of 16 chunks per row staged and read), so the 256 threads still
+// stage two rows of one 16-byte chunk each; no MFMA work is padded.
+template <int D>
+constexpr int kLayoutD = D == 96 ? 128 : D;
 
 // Per head dimension D and tile width BN: the key tile and its LDS layout.
 template <int D, int BN_>
@@ -97,12 +105,14 @@ struct Tile {
 };
 
 template <typename E, int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, D == 256 ? 1 : D == 128 ? 3 : 2) void attn_fwd_kernel(
+__global__ __launch_bounds__(kThreads, D == 256 ? 1 : D >= 96 ? 3 : 2) void attn_fwd_kernel(
     const E* __restrict__ Q, const E* __restrict__ K,
     const E* __restrict__ V, E* __restrict__ O,
     float* __restrict__ LSE, int BH, int Nq, int Nk, int nq, float c) {
-  using T = Tile<D, kBlockN<D>>;
+  using T = Tile<kLayoutD<D>, kBlockN<D>>;
   constexpr int BN = T::BN, KS = T::KS, CPR = T::CPR, KPT = T::KPT, NKB = T::NKB;
+  // Chunks of a row that hold data (all but the layout's padding at d = 96).
+  constexpr int CPR_DATA = D / 8;
   typedef typename Elem<E>::v8 v8;
   typedef typename Elem<E>::v4 v4;
   __shared__ __attribute__((aligned(16))) E smem[T::LDS_ELEMS];
@@ -169,12 +179,15 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : D == 128 ? 3 : 2) void att
   const uint32_t voff = (uint32_t)(kr_v * D + 8 * dc_v) * 2;
   u32x4 kst[KPT], vst[KPT];
 
+  // Chunks past the data (d = 96) are neither loaded nor read back.
+  const bool k_data = CPR_DATA == CPR || dc_k < CPR_DATA;
+  const bool v_data = CPR_DATA == CPR || dc_v < CPR_DATA;
   auto gload = [&](int k0) {
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
       const uint32_t row = (uint32_t)((k0 + i) * D * 2);
-      kst[i] = load16(rk, koff + row);
-      vst[i] = load16(rv, voff + row);
+      if (k_data) kst[i] = load16(rk, koff + row);
+      if (v_data) vst[i] = load16(rv, voff + row);
     }
   };
   // Per-lane LDS byte offsets that do not change with the tile.
@@ -206,9 +219,12 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : D == 128 ? 3 : 2) void att
   // keys kr_v.. contiguous in the permuted slice order -> one write per column.
   auto lds_store = [&](auto stage_c) {
     constexpr uint32_t base = decltype(stage_c)::value * T::STAGE * 2;
+    if (k_data) {
 #pragma unroll
-    for (int i = 0; i < KPT; ++i)
-      *reinterpret_cast<u32x4*>(lds + base + k_wr + i * KS * 2) = kst[i];
+      for (int i = 0; i < KPT; ++i)
+        *reinterpret_cast<u32x4*>(lds + base + k_wr + i * KS * 2) = kst[i];
+    }
+    if (!v_data) return;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int w = e >> 1;  // the same word for column e and e ^ 1
@@ -375,14 +391,14 @@ struct Shape {
 
 template <int D>
 void tile_info(Shape* sh) {
-  sh->lds = Tile<D, kBlockN<D>>::LDS_BYTES;
+  sh->lds = Tile<kLayoutD<D>, kBlockN<D>>::LDS_BYTES;
   sh->block_n = kBlockN<D>;
 }
 
 // Sizes shared by every entry point; Nk only bounds the key tensors.
 int check_sizes(int B, int H, int Nq, int Nk, int d, Shape* sh) {
   if (B < 0 || H < 0 || Nq < 0 || Nk < 0) return ATTN_ERR_SHAPE;
-  if (d != 32 && d != 64 && d != 128 && d != 256) return ATTN_ERR_HEADDIM;
+  if (d != 32 && d != 64 && d != 96 && d != 128 && d != 256) return ATTN_ERR_HEADDIM;
   // One head's tensors are addressed with 32-bit byte offsets (plus one tile).
   if ((int64_t)Nq * d * 2 + (int64_t)kBlockM * d * 2 > INT32_MAX) return ATTN_ERR_SHAPE;
   if ((int64_t)Nk * d * 2 + (int64_t)128 * d * 2 > INT32_MAX) return ATTN_ERR_SHAPE;
@@ -395,6 +411,7 @@ int check_sizes(int B, int H, int Nq, int Nk, int d, Shape* sh) {
   switch (d) {
     case 32: tile_info<32>(sh); break;
     case 64: tile_info<64>(sh); break;
+    case 96: tile_info<96>(sh); break;
     case 128: tile_info<128>(sh); break;
     default: tile_info<256>(sh); break;
   }
@@ -437,6 +454,7 @@ hipError_t launch_type(const Shape& sh, const Args& a, int d, bool causal) {
   switch (d) {
     case 32: return causal ? launch<E, 32, true>(sh, a) : launch<E, 32, false>(sh, a);
     case 64: return causal ? launch<E, 64, true>(sh, a) : launch<E, 64, false>(sh, a);
+    case 96: return causal ? launch<E, 96, true>(sh, a) : launch<E, 96, false>(sh, a);
     case 128: return causal ? launch<E, 128, true>(sh, a) : launch<E, 128, false>(sh, a);
     default: return causal ? launch<E, 256, true>(sh, a) : launch<E, 256, false>(sh, a);
   }
@@ -497,7 +515,7 @@ extern "C" const char* attn_strerror(int status) {
     case ATTN_OK: return "success";
     case ATTN_ERR_NULL: return "null pointer argument";
     case ATTN_ERR_SHAPE: return "invalid shape: sizes must be >= 0 and fit 32-bit head offsets";
-    case ATTN_ERR_HEADDIM: return "unsupported head dimension: d must be 32, 64, 128 or 256";
+    case ATTN_ERR_HEADDIM: return "unsupported head dimension: d must be 32, 64, 96, 128 or 256 (attn_bwd: 64 or 128)";
     case ATTN_ERR_ALIGN: return "misaligned pointer: q, k, v, o need 16 bytes, lse 4 bytes";
     case ATTN_ERR_ALIAS: return "output buffer overlaps an input or the other output";
     case ATTN_ERR_SCALE: return "scale must be finite";
