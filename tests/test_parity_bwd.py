@@ -95,7 +95,7 @@ def check_all(q, k, v, do, scale, causal, what):
 RAGGED = [(1, 1, 1), (1, 2, 17), (2, 3, 100), (1, 1, 129), (2, 2, 300), (1, 3, 513)]
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [32, 64, 96, 128])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("B,H,N", RAGGED)
 def test_bwd_ragged(B, H, N, d, causal):
@@ -108,7 +108,7 @@ def test_bwd_ragged(B, H, N, d, causal):
 CROSS = [(3, 2), (2, 3), (100, 37), (37, 100), (129, 1000), (1000, 129), (200, 1), (1, 200)]
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [32, 64, 96, 128])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("Nq,Nk", CROSS)
 def test_bwd_cross(Nq, Nk, d, causal):
@@ -120,7 +120,7 @@ def test_bwd_cross(Nq, Nk, d, causal):
     check_all(qi["q"], ki["k"], ki["v"], do, qi["scale"], causal, f"cross {Nq}x{Nk}")
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [32, 64, 96, 128])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("N", [100, 300])
 def test_bwd_fp16(N, d, causal):
@@ -244,3 +244,22 @@ def test_bwd_long_causal_sampled():
     assert np.abs(dk64.sum(axis=2)).max() <= 1e-2 * np.abs(dk64).sum(axis=2).max()
     gap = np.abs(dv64.sum(axis=2) - do64.sum(axis=2)).max()
     assert gap <= 1e-2 * max(np.abs(dv64).sum(axis=2).max(), np.abs(do64).sum(axis=2).max())
+
+
+@pytest.mark.parametrize("d", [32, 96])
+def test_bwd_long_other_head_dims(d):
+    """N = 4096 at d = 32 and 96: two heads' every gradient element against
+    the oracle, at full size on the GPU (B=2, H=4)."""
+    announce(f"bwd long d={d}")
+    w = WORKLOADS[3]
+    inp = make_inputs(w, B=2, H=4, N=4096, d=d, seed=21000 + d)
+    do = upstream(inp["q"].shape, 22000 + d, torch.bfloat16)
+    for causal in (False, True):
+        dq, dk, dv, _, _ = run(inp["q"], inp["k"], inp["v"], do, inp["scale"], causal)
+        q64, k64, v64, do64 = (as64(t) for t in (inp["q"], inp["k"], inp["v"], do))
+        for b, h in ((0, 0), (1, 3)):
+            rq, rk, rv = attend_head_grad(q64[b, h], k64[b, h], v64[b, h], do64[b, h],
+                                          inp["scale"], causal)
+            check_grad(dq[b, h], rq, f"({b},{h}) causal={causal} dq")
+            check_grad(dk[b, h], rk, f"({b},{h}) causal={causal} dk")
+            check_grad(dv[b, h], rv, f"({b},{h}) causal={causal} dv")

@@ -52,43 +52,54 @@ using namespace mi_attn;
 constexpr int kBlockRows = 32 * kWaves;  // query rows (dQ) or keys (dK/dV) per workgroup
 
 // Rows per streamed tile (keys in the dQ kernel, queries in the dK/dV
-// kernel): two rows of one 16-byte chunk per thread.
+// kernel).
 template <int D>
-constexpr int kTileRows = D == 64 ? 64 : 32;
+constexpr int kTileRows = D <= 64 ? 64 : 32;
 
-// A tile of BR rows of a [*, D] tensor in LDS: row layout (pitch D + 8, the
+// Head dimension of the LDS tile layout: d = 96 tiles are laid out as
+// d = 128 ones, 12 of 16 chunks per row staged and read (as in the forward).
+template <int D>
+constexpr int kLayoutD = D == 96 ? 128 : D;
+
+// A tile of BR rows of a [*, D] tensor in LDS: row layout (pitch DL + 8, the
 // 16-byte pad spreads the rows read by 8 lanes over distinct bank groups)
-// and transposed layout (D rows of BR, rows of each 16-row slice in
-// slice_pos order, 16-byte blocks swizzled by vt_swz).
+// and transposed layout (DL rows of BR, rows of each 16-row slice in
+// slice_pos order, 16-byte blocks swizzled by vt_swz). A staging thread
+// moves two rows of one 16-byte chunk; at d = 32 half the threads do.
 template <int D, int BR_>
 struct Rows {
+  static constexpr int DL = kLayoutD<D>;
   static constexpr int BR = BR_;
-  static constexpr int KS = D + 8;
+  static constexpr int KS = DL + 8;
   static constexpr int ROW = BR * KS;  // elements, row layout
-  static constexpr int TR = D * BR;    // elements, transposed layout
-  static constexpr int CPR = D / 8;    // 16-byte chunks per row
-  static constexpr int KPT = BR * CPR / kThreads;
-  static constexpr int VG = BR / KPT < 16 ? BR / KPT : 16;
-  static_assert(KPT == 2, "two rows per thread");
-  static_assert(BR % (VG * KPT) == 0 && VG * CPR * (BR / (VG * KPT)) == kThreads,
-                "staging covers the tile exactly once");
+  static constexpr int TR = DL * BR;   // elements, transposed layout
+  static constexpr int CPR = DL / 8;   // 16-byte chunks per row of the layout
+  static constexpr int CPR_DATA = D / 8;  // chunks that hold data
+  static constexpr int STAGERS = BR * CPR / 2;  // threads that stage a tile
+  static constexpr int VG = BR / 2 < 16 ? BR / 2 : 16;
+  static_assert(STAGERS <= kThreads && STAGERS % 64 == 0, "whole waves stage");
+  static_assert(BR % (2 * VG) == 0, "row pairs cover the tile");
 };
 
 // One thread's share of staging a tile: rows kr, kr+1 of chunk dc, with the
 // row group fastest across lanes (VG lanes hold different row pairs of one
 // chunk), loaded with buffer loads (zeros past the end) and written to LDS in
-// row layout, transposed layout, or both.
+// row layout, transposed layout, or both. Threads past STAGERS, and chunks
+// past the data (d = 96), do nothing.
 template <int D, int BR>
 struct Stager {
   using G = Rows<D, BR>;
+  bool active;       // this thread stages a chunk that holds data
   uint32_t goff;     // byte offset of row kr, chunk dc, within a tile
   uint32_t row_wr;   // LDS byte offset, row layout
   uint32_t t_wr[8];  // LDS byte offsets, transposed layout, per column of the chunk
   uint32_t sel_even, sel_odd;
 
   __device__ __forceinline__ explicit Stager(int tid) {
-    const int kr = G::KPT * (tid % G::VG) + G::VG * G::KPT * (tid / (G::VG * G::CPR));
+    const int kr = 2 * (tid % G::VG) + 2 * G::VG * (tid / (G::VG * G::CPR));
     const int dc = (tid / G::VG) % G::CPR;
+    active = (G::STAGERS == kThreads || tid < G::STAGERS) &&
+             (G::CPR_DATA == G::CPR || dc < G::CPR_DATA);
     goff = (uint32_t)(kr * D + 8 * dc) * 2;
     row_wr = (uint32_t)(kr * G::KS + 8 * dc) * 2;
     const int pos = 16 * (kr >> 4) + slice_pos(kr & 15);
@@ -107,17 +118,20 @@ struct Stager {
     sel_odd = flip ? 0x05040100u : 0x07060302u;
   }
   __device__ __forceinline__ void load(rsrc_t r, int row0, u32x4 (&st)[2]) const {
+    if (!active) return;
 #pragma unroll
     for (int i = 0; i < 2; ++i) st[i] = load16(r, goff + (uint32_t)((row0 + i) * D * 2));
   }
   __device__ __forceinline__ void store_rows(char* lds, uint32_t base,
                                              const u32x4 (&st)[2]) const {
+    if (!active) return;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
       *reinterpret_cast<u32x4*>(lds + base + row_wr + i * G::KS * 2) = st[i];
   }
   __device__ __forceinline__ void store_trans(char* lds, uint32_t base,
                                               const u32x4 (&st)[2]) const {
+    if (!active) return;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const uint32_t sel = (e & 1) ? sel_odd : sel_even;
@@ -316,6 +330,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(
 // SIMD at d=128); dV alone (S, P, dV) and dK alone (S, dP, dS, dK) each fit
 // two or three waves per SIMD, for one extra recomputation of S.
 enum Part { kBoth = 0, kDV = 1, kDK = 2 };
+template <int D>
+constexpr bool kOnePass = D <= 96;
 
 // LDS stage of the key-side kernel for part P: only the tiles P reads.
 //   Q rows (S = Q K^T) | dO rows (dP) | Q^T (dK) | dO^T (dV) | lse | D (dS)
@@ -577,8 +593,9 @@ hipError_t launch_bwd(const BwdArgs& a) {
     auto go = [&](const void* fn) {
       return hipLaunchKernel(fn, dim3(BH * nk), dim3(kThreads), args, 0, a.stream);
     };
-    // d=64: dK and dV in one pass. d=128: dV, then dK, each in its own pass.
-    if constexpr (D == 64) {
+    // dK and dV in one pass where both accumulators fit two waves per SIMD;
+    // d=128: dV, then dK, each in its own pass.
+    if constexpr (kOnePass<D>) {
       return go(reinterpret_cast<const void*>(&attn_bwd_kv_kernel<E, D, CAUSAL, kBoth>));
     } else {
       const hipError_t err =
@@ -592,8 +609,12 @@ hipError_t launch_bwd(const BwdArgs& a) {
 
 template <typename E>
 hipError_t launch_bwd_type(const BwdArgs& a, int d, bool causal) {
-  if (d == 64) return causal ? launch_bwd<E, 64, true>(a) : launch_bwd<E, 64, false>(a);
-  return causal ? launch_bwd<E, 128, true>(a) : launch_bwd<E, 128, false>(a);
+  switch (d) {
+    case 32: return causal ? launch_bwd<E, 32, true>(a) : launch_bwd<E, 32, false>(a);
+    case 64: return causal ? launch_bwd<E, 64, true>(a) : launch_bwd<E, 64, false>(a);
+    case 96: return causal ? launch_bwd<E, 96, true>(a) : launch_bwd<E, 96, false>(a);
+    default: return causal ? launch_bwd<E, 128, true>(a) : launch_bwd<E, 128, false>(a);
+  }
 }
 
 }  // namespace
@@ -603,7 +624,7 @@ extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void*
                         float* delta, int B, int H, int Nq, int Nk, int d, int dtype,
                         float scale, int causal, void* stream) {
   if (B < 0 || H < 0 || Nq < 0 || Nk < 0) return ATTN_ERR_SHAPE;
-  if (d != 64 && d != 128) return ATTN_ERR_HEADDIM;
+  if (d != 32 && d != 64 && d != 96 && d != 128) return ATTN_ERR_HEADDIM;
   if ((int64_t)Nq * d * 2 + (int64_t)kBlockRows * d * 2 > INT32_MAX) return ATTN_ERR_SHAPE;
   if ((int64_t)Nk * d * 2 + (int64_t)kBlockRows * d * 2 > INT32_MAX) return ATTN_ERR_SHAPE;
   const int64_t BH = (int64_t)B * H;
