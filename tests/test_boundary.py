@@ -281,3 +281,19 @@ def test_bwd_empty_sides(lib):
     assert bwd(lib, Nq=0, q=None, o=None, lse=None, do=None, dq=None, delta=None,
                k=None) == ERR_NULL
     assert bwd(lib, Nk=0, k=None, v=None, dk=None, dv=None, q=None) == ERR_NULL
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """Without libmi_attn.so every entry point raises; nothing falls back."""
+    import torch
+    monkeypatch.setattr(mi, "_LIB_PATH", str(tmp_path / "libmi_attn.so"))
+    monkeypatch.setattr(mi, "_lib", None)
+    q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ImportError):
+        mi.load_library()
+    for call in (lambda: mi.attn_fwd(q, q, q), lambda: mi.attn_fwd_cross(q, q, q),
+                 lambda: mi.attn_fwd_ex(q, q, q),
+                 lambda: mi.attn_bwd(q, q, q, q, torch.zeros(1, 1, 8), q),
+                 lambda: mi.attn_strerror(0), lambda: mi.attn_fwd_launch_shape(1, 1, 8, 64)):
+        with pytest.raises(ImportError):
+            call()
