@@ -26,6 +26,10 @@ FLOP/clk x 2.4 GHz). roofline.traffic (HBM bytes per launch) comes from the rocp
 FETCH_SIZE / WRITE_SIZE summary committed under profiles/, and is null when
 that summary was taken on a different kernel source.
 
+The line also carries the median and minimum of 20 separately timed launches,
+and the peak re-derived from rocminfo (CUs x 4096 FLOP/clk x max engine
+clock) next to the nominal figure.
+
 --copy-calibration MIB runs only a plain device-to-device copy of that many
 MiB (the known-size reference for the FETCH_SIZE / WRITE_SIZE counters) and
 prints its size as JSON.
@@ -40,6 +44,7 @@ import math
 import dataclasses
 import os
 import re
+import subprocess
 import sys
 import time
 
@@ -166,6 +171,27 @@ def parity_sample_bwd(w, inp, dq, rows=16):
     return {"max_abs_ddq_over_max_ref": worst, "ok": worst <= 2e-2}
 
 
+def device_peak():
+    """CUs and max engine clock of the gfx950 agent from rocminfo, and the dense
+    bf16 MFMA peak they give (4096 FLOP per CU per clock). Runs rocminfo as a
+    child process, so it must be called before this process touches the GPU.
+    None if rocminfo is unavailable."""
+    try:
+        out = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=60).stdout
+    except (OSError, subprocess.SubprocessError):
+        return None
+    for block in out.split("Agent ")[1:]:
+        if "gfx950" not in block:
+            continue
+        cus = re.search(r"Compute Unit:\s+(\d+)", block)
+        mhz = re.search(r"Max Clock Freq\. \(MHz\):\s+(\d+)", block)
+        if cus and mhz:
+            c, m = int(cus.group(1)), int(mhz.group(1))
+            return {"compute_units": c, "max_sclk_mhz": m,
+                    "bf16_tflops": round(c * 4096 * m * 1e6 / 1e12, 1)}
+    return None
+
+
 def copy_calibration(mib):
     import torch
     n = mib * (1 << 20)
@@ -193,6 +219,9 @@ def main():
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
+    peak_check = None
+    if args.gpus == 1 and world == 1 and not args.copy_calibration:
+        peak_check = device_peak()  # before anything touches the GPU
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: the attention forward is built and "
               "measured on a single MI355X (each head is independent; sharding "
@@ -276,6 +305,15 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     event_ms = ev0.elapsed_time(ev1)
+    # Per-launch times, each launch between its own pair of events.
+    per = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(20)]
+    for a, b in per:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    per_us = sorted(a.elapsed_time(b) * 1e3 for a, b in per)
 
     flops = attn_flops(w.B, w.H, w.N, w.d, w.causal) * (2.5 if backward else 1.0)
     launch_s = event_ms / 1e3 / args.steps
@@ -317,6 +355,9 @@ def main():
         "cpu_baseline": cpu,
         "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "kernel_avg_us": round(launch_s * 1e6, 2),
+        "launch_us_median": round(per_us[len(per_us) // 2], 2),
+        "launch_us_min": round(per_us[0], 2),
+        "peak_check": peak_check,
         "parity_sample": parity,
         "kernel_source_sha256_16": kernel_sha(args.which),
     }
