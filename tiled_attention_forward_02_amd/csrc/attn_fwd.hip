@@ -62,6 +62,12 @@ constexpr float kLazySum = 4096.f;  // largest per-lane tile sum kept on a stale
 // d = 64 workloads (B=4, H=16, N=1024 and causal B=8, H=16, N=2048).
 template <int D>
 constexpr bool kSpeculativeWeights = D != 64;
+// Raise a wave's priority while it issues its two MFMA chains (and drop it
+// for the softmax and the staging), so that when several waves of a SIMD
+// have work the matrix pipe is fed first: +1.2-2.2% at d = 128 (measured
+// interleaved against the plain kernel), not kept at d <= 64 (0 to -3%).
+template <int D>
+constexpr bool kMfmaPriority = D >= 96;
 
 constexpr int kBlockM = 32 * kWaves;   // query rows per workgroup
 // Keys per tile for head dimension D. At d=128 a 32-key tile keeps a wave
@@ -257,6 +263,7 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : D >= 96 ? 3 : 2) void attn
     if (has_next) gload(k0 + BN);
 
     if (k0 < wave_kv_end) {
+      if constexpr (kMfmaPriority<D>) __builtin_amdgcn_s_setprio(1);
       // S^T = K * Q^T: NKB blocks of 32 keys, one MFMA chain each.
       f32x16 sacc[NKB];
 #pragma unroll
@@ -270,6 +277,7 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : D >= 96 ? 3 : 2) void attn
         }
       }
 
+      if constexpr (kMfmaPriority<D>) __builtin_amdgcn_s_setprio(0);
       // Keys past the end and (causal) keys after the query get -inf.
       if ((k0 + BN > Nk) || (CAUSAL && k0 + BN - 1 > qw + off)) {
 #pragma unroll
@@ -333,6 +341,7 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : D >= 96 ? 3 : 2) void attn
       }
       l_run += tsum;
 
+      if constexpr (kMfmaPriority<D>) __builtin_amdgcn_s_setprio(1);
       // O^T += V^T * P^T, 16 keys per MFMA.
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
@@ -347,6 +356,7 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : D >= 96 ? 3 : 2) void attn
         }
     }
 
+    if constexpr (kMfmaPriority<D>) __builtin_amdgcn_s_setprio(0);
     if (has_next) lds_store(std::integral_constant<int, stage ^ 1>{});
     __syncthreads();
   };
