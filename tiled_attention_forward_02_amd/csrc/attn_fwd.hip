@@ -58,10 +58,11 @@ constexpr float kLazyMax = 8.0f;  // tolerated growth of the row max, log2 units
 constexpr float kLazySum = 4096.f;  // largest per-lane tile sum kept on a stale max
 // Softmax weights first, row maximum only when they grow too large, or row
 // maximum first. Weights first saves the max reduction: measured faster at
-// d = 32 (where the softmax dominates), 96, 128 and 256, and slower on the
-// d = 64 workloads (B=4, H=16, N=1024 and causal B=8, H=16, N=2048).
+// d = 96, 128 and 256; slower at d = 32 (-0.9% to -3.4%) and on the d = 64
+// workloads (B=4, H=16, N=1024 and causal B=8, H=16, N=2048), where the
+// extra live scores cost more than the reduction.
 template <int D>
-constexpr bool kSpeculativeWeights = D != 64;
+constexpr bool kSpeculativeWeights = D >= 96;
 // Raise a wave's priority while it issues its two MFMA chains (and drop it
 // for the softmax and the staging), so that when several waves of a SIMD
 // have work the matrix pipe is fed first: +1.2-2.2% at d = 128 (measured
