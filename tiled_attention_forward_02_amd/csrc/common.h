@@ -64,12 +64,13 @@ __device__ __forceinline__ int slice_pos(int o) {
 
 // XOR swizzle of the 16-byte blocks of a transposed tile's row (BN/8 blocks),
 // a function of the row index mod 32 only (the same for every 32-row block a
-// lane reads): any 8 aligned consecutive rows, and any 16, land on distinct
-// bank groups, whether a row is 128 bytes (BN = 64) or 64 bytes (BN = 32).
+// lane reads). Chosen by measurement (SQ_LDS_BANK_CONFLICT on gfx950): with
+// 64-byte rows (BN = 32) any function of bits 0, 1, 3 alone left 4 conflict
+// cycles on every 8-cycle operand read; keying on bit 2 removes them all.
 template <int BN>
 __device__ __forceinline__ int vt_swz(int d) {
   d &= 31;
-  return BN >= 64 ? ((d ^ (d >> 3)) & 7) : (((d >> 1) ^ (d >> 3)) & 3);
+  return BN >= 64 ? ((d ^ (d >> 3)) & 7) : ((d >> 2) & 3);
 }
 
 // Workgroup id -> (batch*head, tile). Workgroups are dealt to the 8 XCDs
