@@ -6,6 +6,7 @@ The shared library lands next to this file, where the binding loads it.
 
 from __future__ import annotations
 
+import ctypes
 import os
 import shutil
 import subprocess
@@ -60,6 +61,17 @@ def _run(cmd, verbose):
         print(err, file=sys.stderr)
 
 
+def _check_links(path):
+    """Refuse a library with unresolved symbols. A kernel whose host stub the
+    compiler did not emit leaves its launch undefined without any diagnostic;
+    the library then fails only when loaded."""
+    try:
+        ctypes.CDLL(path, mode=os.RTLD_NOW)
+    except OSError as e:
+        os.unlink(path)
+        raise RuntimeError(f"built library does not load: {e}") from None
+
+
 def build(verbose=False):
     """Compile the HIP sources into libmi_attn.so (always recompiles)."""
     with tempfile.TemporaryDirectory(prefix="mi_attn_build_") as tmpdir:
@@ -70,6 +82,7 @@ def build(verbose=False):
             objs.append(obj)
         tmp = LIB + ".tmp"
         _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
+    _check_links(tmp)
     os.replace(tmp, LIB)
     return LIB
 

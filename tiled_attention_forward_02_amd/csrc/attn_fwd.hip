@@ -13,7 +13,8 @@
 // workgroups share a CU, so each SIMD holds waves of different workgroups
 // whose softmax (VALU) and matrix (MFMA) phases interleave. Keys and values
 // stream through LDS in tiles of 32 (d=128) or 64 (d=64) keys, HBM ->
-// registers -> LDS, double buffered one tile ahead with one barrier per tile.
+// registers -> LDS (K at d = 96 and 256 by buffer loads that write LDS
+// directly), double buffered one tile ahead with one barrier per tile.
 // Global loads are buffer loads: rows past N come back as zeros, with no
 // branches. Both contractions run on v_mfma_f32_32x32x16_bf16 in transposed
 // form:
@@ -69,6 +70,13 @@ constexpr bool kSpeculativeWeights = D >= 96;
 // interleaved against the plain kernel), not kept at d <= 64 (0 to -3%).
 template <int D>
 constexpr bool kMfmaPriority = D >= 96;
+// Stage K by buffer loads that write LDS directly (no registers, no LDS
+// write instructions) instead of through registers. Measured interleaved
+// against the register path: +2.0% at d = 96 and +3.1% at d = 256; -0.7%
+// at d = 128, -1% at d = 32, and -5 to -7% on the d = 64 workloads, whose
+// causal kernel it pushes past 128 VGPRs (four waves per SIMD down to three).
+template <int D>
+constexpr bool kKDma = D == 96 || D == 256;
 
 constexpr int kBlockM = 32 * kWaves;   // query rows per workgroup
 // Keys per tile for head dimension D. At d=128 a 32-key tile keeps a wave
@@ -172,12 +180,50 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : D >= 96 ? 3 : 2) void attn
   const int nt = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
   const int wave_kv_end = CAUSAL ? min(Nk, qw + 32 + off) : Nk;
 
-  // Staging. K: thread owns rows kr_k .. +KPT-1, 16-byte chunk dc_k, with the
-  // chunk fastest across lanes (a row per CPR lanes: coalesced loads,
-  // contiguous LDS writes). V: the key group fastest across lanes, so the VG
-  // lanes of one transposed LDS write cover VG different key groups of one
-  // column (distinct banks) and a wave's load still reads 64/VG adjacent
-  // chunks (1024/VG contiguous bytes) of each row it touches.
+  char* const lds = reinterpret_cast<char*>(smem);
+
+  // Staging of K, DMA form: straight from HBM into LDS (16 bytes a lane, no
+  // registers). A K tile in LDS is BN rows of CPR + 1 16-byte
+  // slots (the last one the row's pad); one wave instruction writes 64
+  // consecutive slots at its LDS base, lane l the slot 64 u + l of
+  // instruction u. Each lane's (row, chunk) for its slots is fixed; pad slots
+  // and chunks past the data (d = 96) are masked off. The tile's first key
+  // goes into the vector offset, so the buffer range check still zero-fills
+  // rows past Nk.
+  constexpr int KROW_SLOTS = CPR + 1;
+  constexpr int KSLOTS = BN * KROW_SLOTS;
+  constexpr int KINSTR = (KSLOTS + 63) / 64;                 // per tile
+  constexpr int KI_W = (KINSTR + kWaves - 1) / kWaves;       // per wave, at most
+  static_assert(KSLOTS * 8 == T::K_ELEMS, "K slots tile the padded K layout");
+  uint32_t kdma_off[KI_W];
+  bool kdma_on[KI_W];
+#pragma unroll
+  for (int i = 0; i < KI_W; ++i) {
+    const int u = wave + kWaves * i;
+    const int slot = 64 * u + lane;
+    const int row = slot / KROW_SLOTS, ch = slot % KROW_SLOTS;
+    kdma_on[i] = u < KINSTR && slot < KSLOTS && ch < CPR_DATA;
+    kdma_off[i] = (uint32_t)(row * D + 8 * ch) * 2;
+  }
+  auto kdma = [&](auto stage_c, int k0) {
+    if constexpr (!kKDma<D>) return;
+    constexpr uint32_t base = decltype(stage_c)::value * T::STAGE * 2;
+#pragma unroll
+    for (int i = 0; i < KI_W; ++i) {
+      const int u = wave + kWaves * i;
+      if (u < KINSTR && kdma_on[i])
+        load16_lds(rk, lds + base + 1024 * u, kdma_off[i] + (uint32_t)k0 * D * 2);
+    }
+  };
+
+  // Staging through registers. K, register form: thread owns rows
+  // kr_k .. +KPT-1, 16-byte chunk dc_k, with the chunk fastest across lanes
+  // (a row per CPR lanes: coalesced loads, contiguous LDS writes). V, always
+  // through registers, transposed on the way into LDS: the key group is
+  // fastest across lanes, so the VG lanes of one transposed LDS write cover
+  // VG different key groups of one column (distinct banks) and a wave's load
+  // still reads 64/VG adjacent chunks (1024/VG contiguous bytes) of each row
+  // it touches.
   constexpr int VG = T::VG;
   const int kr_k = KPT * (tid / CPR);
   const int dc_k = tid % CPR;
@@ -188,7 +234,7 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : D >= 96 ? 3 : 2) void attn
   u32x4 kst[KPT], vst[KPT];
 
   // Chunks past the data (d = 96) are neither loaded nor read back.
-  const bool k_data = CPR_DATA == CPR || dc_k < CPR_DATA;
+  const bool k_data = !kKDma<D> && (CPR_DATA == CPR || dc_k < CPR_DATA);
   const bool v_data = CPR_DATA == CPR || dc_v < CPR_DATA;
   auto gload = [&](int k0) {
 #pragma unroll
@@ -223,9 +269,9 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : D >= 96 ? 3 : 2) void attn
   for (int g = 0; g < BN / 16; ++g)
     v_rd[g] = (uint32_t)(T::K_ELEMS + col * BN + ((2 * g + half) ^ vt_swz<BN>(col)) * 8) * 2;
 
-  char* const lds = reinterpret_cast<char*>(smem);
-  // K rows as they are; V^T with, for each of the chunk's 8 columns d, the KPT
-  // keys kr_v.. contiguous in the permuted slice order -> one write per column.
+  // K rows as they are (register form); V^T with, for each of the chunk's 8
+  // columns d, the KPT keys kr_v.. contiguous in the permuted slice order ->
+  // one write per column.
   auto lds_store = [&](auto stage_c) {
     constexpr uint32_t base = decltype(stage_c)::value * T::STAGE * 2;
     if (k_data) {
@@ -262,7 +308,10 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : D >= 96 ? 3 : 2) void attn
     constexpr uint32_t base = stage * T::STAGE * 2;
     const int k0 = t * BN;
     const bool has_next = t + 1 < nt;
-    if (has_next) gload(k0 + BN);
+    if (has_next) {
+      kdma(std::integral_constant<int, stage ^ 1>{}, k0 + BN);
+      gload(k0 + BN);
+    }
 
     if (k0 < wave_kv_end) {
       if constexpr (kMfmaPriority<D>) __builtin_amdgcn_s_setprio(1);
@@ -360,11 +409,16 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : D >= 96 ? 3 : 2) void attn
 
     if constexpr (kMfmaPriority<D>) __builtin_amdgcn_s_setprio(0);
     if (has_next) lds_store(std::integral_constant<int, stage ^ 1>{});
+    // DMA form: the next tile's K lands in LDS with no instruction of this
+    // wave writing it; wait for the loads before the barrier.
+    if constexpr (kKDma<D>) __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
 
+  kdma(std::integral_constant<int, 0>{}, 0);
   gload(0);
   lds_store(std::integral_constant<int, 0>{});
+  if constexpr (kKDma<D>) __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   for (int t = 0; t < nt; t += 2) {
     step(t, std::integral_constant<int, 0>{});

@@ -110,6 +110,15 @@ __device__ __forceinline__ u32x4 load16(rsrc_t r, uint32_t byte_off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 0);
 }
 
+// 16 bytes per lane from the buffer at byte_off straight into LDS, no
+// registers: the wave's 64 lanes fill the 1024 bytes at lds_base in lane
+// order (lane l at lds_base + 16 l). The range check applies as for load16.
+// Completion is counted by vmcnt, like any buffer load.
+__device__ __forceinline__ void load16_lds(rsrc_t r, char* lds_base, uint32_t byte_off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      r, (__attribute__((address_space(3))) void*)lds_base, 16, (int)byte_off, 0, 0, 0);
+}
+
 // Value of x in the lane 32 positions away, combined with op (same result in
 // both lanes of the pair, bit for bit).
 __device__ __forceinline__ float swap_halves_max(float x) {
