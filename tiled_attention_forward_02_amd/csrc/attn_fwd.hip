@@ -26,7 +26,9 @@
 // statistics are per-lane scalars plus one swap between the two 32-lane
 // halves, and the S^T accumulator rounded to bf16 is already the B operand of
 // the P*V product, given a fixed permutation of the key order inside each
-// 16-key slice. V^T is written to LDS in that permuted order.
+// 16-key slice. V stays row-major in LDS; transposing LDS reads
+// (ds_read_b64_tr_b16) hand each lane the V^T column it needs, 4 keys at a
+// time, in that permuted order.
 //
 // The running maximum is raised lazily: only when a tile's row maximum
 // exceeds it by more than 2^8 (log2 units) are O and the row sum rescaled;
@@ -106,18 +108,18 @@ struct Tile {
   static constexpr int NKB = BN / 32;            // 32-key MFMA blocks per tile
   static constexpr int KS = D + 8;               // K row pitch in LDS (bf16), 16 B pad
   static constexpr int K_ELEMS = BN * KS;        // one K tile
-  static constexpr int VT_ELEMS = D * BN;        // one V^T tile
+  // V row pitch in LDS (elements): an odd multiple of 32 bytes, so the
+  // 4 consecutive rows x 32 bytes that a 16-lane group of a transposing read
+  // touches fall in distinct 32-byte slots of a 128-byte bank row.
+  static constexpr int VS = D + 16;
+  static constexpr int V_ELEMS = BN * VS;        // one V tile, row-major
   static constexpr int CPR = D / 8;              // 16-byte chunks per row
   static constexpr int KPT = BN * CPR / kThreads;  // rows each thread stages (4 or 2)
-  // V staging: key groups of KPT keys spread over VG consecutive lanes (16,
-  // or fewer when the tile has fewer groups), then the 16-byte chunk.
-  static constexpr int VG = BN / KPT < 16 ? BN / KPT : 16;
-  static constexpr int STAGE = K_ELEMS + VT_ELEMS;
+  static constexpr int STAGE = K_ELEMS + V_ELEMS;
   static constexpr int LDS_ELEMS = 2 * STAGE;
   static constexpr int LDS_BYTES = 2 * LDS_ELEMS;
   static_assert(KPT == 2 || KPT == 4, "staging layout");
-  static_assert(BN % (VG * KPT) == 0 && VG * CPR * (BN / (VG * KPT)) == kThreads,
-                "V staging covers the tile exactly once");
+  static_assert((VS * 2) % 64 == 32, "V pitch");
 };
 
 template <typename E, int D, bool CAUSAL>
@@ -216,81 +218,45 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : D >= 96 ? 3 : 2) void attn
     }
   };
 
-  // Staging through registers. K, register form: thread owns rows
-  // kr_k .. +KPT-1, 16-byte chunk dc_k, with the chunk fastest across lanes
-  // (a row per CPR lanes: coalesced loads, contiguous LDS writes). V, always
-  // through registers, transposed on the way into LDS: the key group is
-  // fastest across lanes, so the VG lanes of one transposed LDS write cover
-  // VG different key groups of one column (distinct banks) and a wave's load
-  // still reads 64/VG adjacent chunks (1024/VG contiguous bytes) of each row
-  // it touches.
-  constexpr int VG = T::VG;
-  const int kr_k = KPT * (tid / CPR);
-  const int dc_k = tid % CPR;
-  const int kr_v = KPT * (tid % VG) + VG * KPT * (tid / (VG * CPR));
-  const int dc_v = (tid / VG) % CPR;
-  const uint32_t koff = (uint32_t)(kr_k * D + 8 * dc_k) * 2;
-  const uint32_t voff = (uint32_t)(kr_v * D + 8 * dc_v) * 2;
+  // Staging through registers: thread owns rows kr .. kr+KPT-1 and 16-byte
+  // chunk dc of both K (register form) and V, the chunk fastest across lanes
+  // (a row per CPR lanes: coalesced loads, contiguous 16-byte LDS writes).
+  // Both tiles stay row-major in LDS; the V^T operand comes from
+  // transposing reads.
+  const int kr = KPT * (tid / CPR);
+  const int dc = tid % CPR;
+  const uint32_t goff = (uint32_t)(kr * D + 8 * dc) * 2;
   u32x4 kst[KPT], vst[KPT];
 
   // Chunks past the data (d = 96) are neither loaded nor read back.
-  const bool k_data = !kKDma<D> && (CPR_DATA == CPR || dc_k < CPR_DATA);
-  const bool v_data = CPR_DATA == CPR || dc_v < CPR_DATA;
+  const bool v_data = CPR_DATA == CPR || dc < CPR_DATA;
+  const bool k_data = !kKDma<D> && v_data;
   auto gload = [&](int k0) {
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
       const uint32_t row = (uint32_t)((k0 + i) * D * 2);
-      if (k_data) kst[i] = load16(rk, koff + row);
-      if (v_data) vst[i] = load16(rv, voff + row);
+      if (k_data) kst[i] = load16(rk, goff + row);
+      if (v_data) vst[i] = load16(rv, goff + row);
     }
   };
   // Per-lane LDS byte offsets that do not change with the tile.
-  const uint32_t k_wr = (uint32_t)(kr_k * KS + 8 * dc_k) * 2;
-  const int vpos = 16 * (kr_v >> 4) + slice_pos(kr_v & 15);
-  // With 64-byte V^T rows (32-key tiles), odd VG-lane groups write the
-  // chunk's columns in the order e ^ 1, so neighbouring groups write rows of
-  // opposite parity instead of the same banks (measured at d=128: without it
-  // the transposed writes take 67 M bank-conflict cycles per launch of the
-  // B=16, H=16, N=4096 workload, with it none).
-  const int vflip = BN == 32 ? (tid / VG) & 1 : 0;
-  uint32_t v_wr[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int d = 8 * dc_v + (e ^ vflip);
-    v_wr[e] = (uint32_t)(T::K_ELEMS + d * BN + ((vpos >> 3) ^ vt_swz<BN>(d)) * 8 + (vpos & 7)) * 2;
-  }
-  // v_perm selectors for the bf16 at an even (0x05040100) or odd (0x07060302)
-  // column of a 32-bit word, swapped for the flipped lane groups.
-  const uint32_t sel_even = vflip ? 0x07060302u : 0x05040100u;
-  const uint32_t sel_odd = vflip ? 0x05040100u : 0x07060302u;
+  const uint32_t k_wr = (uint32_t)(kr * KS + 8 * dc) * 2;
+  const uint32_t v_wr = (uint32_t)(T::K_ELEMS + kr * T::VS + 8 * dc) * 2;
   const uint32_t k_rd = (uint32_t)(col * KS + 8 * half) * 2;
-  uint32_t v_rd[BN / 16];  // V^T read of 16-key slice g, rows 32*db + col (db: immediate)
-#pragma unroll
-  for (int g = 0; g < BN / 16; ++g)
-    v_rd[g] = (uint32_t)(T::K_ELEMS + col * BN + ((2 * g + half) ^ vt_swz<BN>(col)) * 8) * 2;
+  // V^T fragment of a 16-key slice and 32 columns: two transposing reads, 8
+  // keys apart. Lane 16 g + s points at row 4 (g / 2) + s / 4, columns
+  // 16 (g % 2) + 4 (s % 4) .. +3 of the slice; it then holds column
+  // col of keys 4 half .. 4 half + 3 (and 8 further with the second read),
+  // the keys its P^T register slots carry (see slice_pos).
+  const uint32_t v_rd = (uint32_t)(T::K_ELEMS + (4 * half + ((lane & 15) >> 2)) * T::VS +
+                                   16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
 
-  // K rows as they are (register form); V^T with, for each of the chunk's 8
-  // columns d, the KPT keys kr_v.. contiguous in the permuted slice order ->
-  // one write per column.
   auto lds_store = [&](auto stage_c) {
     constexpr uint32_t base = decltype(stage_c)::value * T::STAGE * 2;
-    if (k_data) {
 #pragma unroll
-      for (int i = 0; i < KPT; ++i)
-        *reinterpret_cast<u32x4*>(lds + base + k_wr + i * KS * 2) = kst[i];
-    }
-    if (!v_data) return;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int w = e >> 1;  // the same word for column e and e ^ 1
-      const uint32_t sel = (e & 1) ? sel_odd : sel_even;
-      const uint32_t lo = __builtin_amdgcn_perm(vst[1][w], vst[0][w], sel);
-      if constexpr (KPT == 4) {
-        const uint32_t hi = __builtin_amdgcn_perm(vst[3][w], vst[2][w], sel);
-        *reinterpret_cast<u32x2*>(lds + base + v_wr[e]) = u32x2{lo, hi};
-      } else {
-        *reinterpret_cast<uint32_t*>(lds + base + v_wr[e]) = lo;
-      }
+    for (int i = 0; i < KPT; ++i) {
+      if (k_data) *reinterpret_cast<u32x4*>(lds + base + k_wr + i * KS * 2) = kst[i];
+      if (v_data) *reinterpret_cast<u32x4*>(lds + base + v_wr + i * T::VS * 2) = vst[i];
     }
   };
 
@@ -400,8 +366,9 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : D >= 96 ? 3 : 2) void attn
         for (int sg = 0; sg < 2; ++sg) {
 #pragma unroll
           for (int db = 0; db < D / 32; ++db) {
-            const v8 a = *reinterpret_cast<const v8*>(
-                lds + base + v_rd[2 * kb + sg] + 32 * db * BN * 2);
+            const char* p = lds + base + v_rd + ((32 * kb + 16 * sg) * T::VS + 32 * db) * 2;
+            const u32x2 lo = lds_read_tr16(p), hi = lds_read_tr16(p + 8 * T::VS * 2);
+            const v8 a = __builtin_bit_cast(v8, u32x4{lo[0], lo[1], hi[0], hi[1]});
             oacc[db] = Elem<E>::mfma(a, pb[kb][sg], oacc[db]);
           }
         }

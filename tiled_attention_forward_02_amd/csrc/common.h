@@ -119,6 +119,17 @@ __device__ __forceinline__ void load16_lds(rsrc_t r, char* lds_base, uint32_t by
       r, (__attribute__((address_space(3))) void*)lds_base, 16, (int)byte_off, 0, 0, 0);
 }
 
+// Transposing LDS read of 16-bit data (ds_read_b64_tr_b16). Each lane gives
+// the address of 4 consecutive elements (8 bytes). Within each group of 16
+// lanes, lane 4a + b receives, as its element e, element b of the 4 given by
+// lane a + 4e of the group (checked on gfx950 with a layout probe).
+__device__ __forceinline__ u32x2 lds_read_tr16(const char* p) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(p));
+  return __builtin_bit_cast(u32x2, r);
+}
+
 // Value of x in the lane 32 positions away, combined with op (same result in
 // both lanes of the pair, bit for bit).
 __device__ __forceinline__ float swap_halves_max(float x) {
