@@ -72,13 +72,18 @@ constexpr bool kSpeculativeWeights = D >= 96;
 // interleaved against the plain kernel), not kept at d <= 64 (0 to -3%).
 template <int D>
 constexpr bool kMfmaPriority = D >= 96;
-// Stage K by buffer loads that write LDS directly (no registers, no LDS
-// write instructions) instead of through registers. Measured interleaved
-// against the register path: +2.0% at d = 96 and +3.1% at d = 256; -0.7%
-// at d = 128, -1% at d = 32, and -5 to -7% on the d = 64 workloads, whose
-// causal kernel it pushes past 128 VGPRs (four waves per SIMD down to three).
+// Stage K and V by buffer loads that write LDS directly (no registers, no
+// LDS write instructions) instead of through registers. Timing copies that
+// drop the global loads but keep the LDS writes ran 16% faster at d = 128:
+// the loads into registers, not their latency, were the cost. Measured
+// interleaved against the register path: K and V by DMA +2.2% at d = 128,
+// +3.8% on the long causal workload, +7.5% at d = 96 (its kernel drops to
+// 127 VGPRs, four waves per SIMD); at d = 256 K alone (+3.1%; V too -2.9%);
+// at d = 32 and 64 neither (-1% to -4%).
 template <int D>
-constexpr bool kKDma = D == 96 || D == 256;
+constexpr bool kKDma = D == 96 || D == 128 || D == 256;
+template <int D>
+constexpr bool kVDma = D == 96 || D == 128;
 
 constexpr int kBlockM = 32 * kWaves;   // query rows per workgroup
 // Keys per tile for head dimension D. At d=128 a 32-key tile keeps a wave
@@ -184,37 +189,49 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : D >= 96 ? 3 : 2) void attn
 
   char* const lds = reinterpret_cast<char*>(smem);
 
-  // Staging of K, DMA form: straight from HBM into LDS (16 bytes a lane, no
-  // registers). A K tile in LDS is BN rows of CPR + 1 16-byte
-  // slots (the last one the row's pad); one wave instruction writes 64
+  // Staging by DMA: straight from HBM into LDS (16 bytes a lane, no
+  // registers). A tile in LDS is BN rows of row_slots 16-byte slots (the
+  // row's data chunks, then its pad); one wave instruction writes 64
   // consecutive slots at its LDS base, lane l the slot 64 u + l of
   // instruction u. Each lane's (row, chunk) for its slots is fixed; pad slots
   // and chunks past the data (d = 96) are masked off. The tile's first key
   // goes into the vector offset, so the buffer range check still zero-fills
   // rows past Nk.
-  constexpr int KROW_SLOTS = CPR + 1;
-  constexpr int KSLOTS = BN * KROW_SLOTS;
-  constexpr int KINSTR = (KSLOTS + 63) / 64;                 // per tile
-  constexpr int KI_W = (KINSTR + kWaves - 1) / kWaves;       // per wave, at most
-  static_assert(KSLOTS * 8 == T::K_ELEMS, "K slots tile the padded K layout");
-  uint32_t kdma_off[KI_W];
-  bool kdma_on[KI_W];
+  constexpr int KROW_SLOTS = KS / 8, VROW_SLOTS = T::VS / 8;
+  constexpr int KINSTR = (BN * KROW_SLOTS + 63) / 64;      // per tile
+  constexpr int VINSTR = (BN * VROW_SLOTS + 63) / 64;
+  constexpr int KI_W = (KINSTR + kWaves - 1) / kWaves;     // per wave, at most
+  constexpr int VI_W = (VINSTR + kWaves - 1) / kWaves;
+  uint32_t kdma_off[KI_W], vdma_off[VI_W];
+  bool kdma_on[KI_W], vdma_on[VI_W];
 #pragma unroll
   for (int i = 0; i < KI_W; ++i) {
-    const int u = wave + kWaves * i;
-    const int slot = 64 * u + lane;
+    const int u = wave + kWaves * i, slot = 64 * u + lane;
     const int row = slot / KROW_SLOTS, ch = slot % KROW_SLOTS;
-    kdma_on[i] = u < KINSTR && slot < KSLOTS && ch < CPR_DATA;
+    kdma_on[i] = u < KINSTR && slot < BN * KROW_SLOTS && ch < CPR_DATA;
     kdma_off[i] = (uint32_t)(row * D + 8 * ch) * 2;
   }
-  auto kdma = [&](auto stage_c, int k0) {
-    if constexpr (!kKDma<D>) return;
-    constexpr uint32_t base = decltype(stage_c)::value * T::STAGE * 2;
 #pragma unroll
-    for (int i = 0; i < KI_W; ++i) {
-      const int u = wave + kWaves * i;
-      if (u < KINSTR && kdma_on[i])
-        load16_lds(rk, lds + base + 1024 * u, kdma_off[i] + (uint32_t)k0 * D * 2);
+  for (int i = 0; i < VI_W; ++i) {
+    const int u = wave + kWaves * i, slot = 64 * u + lane;
+    const int row = slot / VROW_SLOTS, ch = slot % VROW_SLOTS;
+    vdma_on[i] = u < VINSTR && slot < BN * VROW_SLOTS && ch < CPR_DATA;
+    vdma_off[i] = (uint32_t)(row * D + 8 * ch) * 2;
+  }
+  auto dma = [&](auto stage_c, int k0) {
+    constexpr uint32_t base = decltype(stage_c)::value * T::STAGE * 2;
+    if constexpr (kKDma<D>) {
+#pragma unroll
+      for (int i = 0; i < KI_W; ++i)
+        if (wave + kWaves * i < KINSTR && kdma_on[i])
+          load16_lds(rk, lds + base + 1024 * (wave + kWaves * i), kdma_off[i] + (uint32_t)k0 * D * 2);
+    }
+    if constexpr (kVDma<D>) {
+#pragma unroll
+      for (int i = 0; i < VI_W; ++i)
+        if (wave + kWaves * i < VINSTR && vdma_on[i])
+          load16_lds(rv, lds + base + T::K_ELEMS * 2 + 1024 * (wave + kWaves * i),
+                     vdma_off[i] + (uint32_t)k0 * D * 2);
     }
   };
 
@@ -229,8 +246,9 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : D >= 96 ? 3 : 2) void attn
   u32x4 kst[KPT], vst[KPT];
 
   // Chunks past the data (d = 96) are neither loaded nor read back.
-  const bool v_data = CPR_DATA == CPR || dc < CPR_DATA;
-  const bool k_data = !kKDma<D> && v_data;
+  const bool data = CPR_DATA == CPR || dc < CPR_DATA;
+  const bool k_data = !kKDma<D> && data;
+  const bool v_data = !kVDma<D> && data;
   auto gload = [&](int k0) {
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
@@ -275,7 +293,7 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : D >= 96 ? 3 : 2) void attn
     const int k0 = t * BN;
     const bool has_next = t + 1 < nt;
     if (has_next) {
-      kdma(std::integral_constant<int, stage ^ 1>{}, k0 + BN);
+      dma(std::integral_constant<int, stage ^ 1>{}, k0 + BN);
       gload(k0 + BN);
     }
 
@@ -378,14 +396,14 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : D >= 96 ? 3 : 2) void attn
     if (has_next) lds_store(std::integral_constant<int, stage ^ 1>{});
     // DMA form: the next tile's K lands in LDS with no instruction of this
     // wave writing it; wait for the loads before the barrier.
-    if constexpr (kKDma<D>) __builtin_amdgcn_s_waitcnt(0);
+    if constexpr (kKDma<D> || kVDma<D>) __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
 
-  kdma(std::integral_constant<int, 0>{}, 0);
+  dma(std::integral_constant<int, 0>{}, 0);
   gload(0);
   lds_store(std::integral_constant<int, 0>{});
-  if constexpr (kKDma<D>) __builtin_amdgcn_s_waitcnt(0);
+  if constexpr (kKDma<D> || kVDma<D>) __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   for (int t = 0; t < nt; t += 2) {
     step(t, std::integral_constant<int, 0>{});
