@@ -29,7 +29,9 @@
 //
 // In both, the C accumulator of P or dS, rounded to the input type, is the B
 // operand of the next product once the rows inside each 16-row slice follow
-// slice_pos(); the transposed LDS tiles are written in that order. Masked
+// slice_pos(). The matching transposed A operands (K^T, Q^T, dO^T) come from
+// transposing LDS reads of a row-major copy of the tile, which hand each
+// lane 4 rows of one column in that order. Masked
 // entries (causal, and keys past Nk in the dQ kernel) get P = 0 by a select
 // after the exponent, so any finite scale works, 0 and negative included.
 // A row with lse = -inf (no visible key) gets P = 0 throughout.
@@ -61,62 +63,48 @@ constexpr int kTileRows = D <= 64 ? 64 : 32;
 template <int D>
 constexpr int kLayoutD = D == 96 ? 128 : D;
 
-// A tile of BR rows of a [*, D] tensor in LDS: row layout (pitch DL + 8, the
-// 16-byte pad spreads the rows read by 8 lanes over distinct bank groups)
-// and transposed layout (DL rows of BR, rows of each 16-row slice in
-// slice_pos order, 16-byte blocks swizzled by vt_swz). A staging thread
-// moves two rows of one 16-byte chunk; at d = 32 half the threads do.
+// A tile of BR rows of a [*, D] tensor in LDS, in up to two row-major
+// copies: pitch DL + 8 for 16-byte row reads (the 16-byte pad spreads the
+// rows read by 8 lanes over distinct bank groups), and pitch DL + 16 for
+// transposing reads (an odd multiple of 32 bytes: the 4 rows x 32 bytes a
+// 16-lane group reads fall in distinct 32-byte slots of a 128-byte bank
+// row). A staging thread moves two rows of one 16-byte chunk; at d = 32 half
+// the threads do.
 template <int D, int BR_>
 struct Rows {
   static constexpr int DL = kLayoutD<D>;
   static constexpr int BR = BR_;
   static constexpr int KS = DL + 8;
-  static constexpr int ROW = BR * KS;  // elements, row layout
-  static constexpr int TR = DL * BR;   // elements, transposed layout
+  static constexpr int TS = DL + 16;
+  static constexpr int ROW = BR * KS;  // elements, copy for row reads
+  static constexpr int TR = BR * TS;   // elements, copy for transposing reads
   static constexpr int CPR = DL / 8;   // 16-byte chunks per row of the layout
   static constexpr int CPR_DATA = D / 8;  // chunks that hold data
   static constexpr int STAGERS = BR * CPR / 2;  // threads that stage a tile
-  static constexpr int VG = BR / 2 < 16 ? BR / 2 : 16;
   static_assert(STAGERS <= kThreads && STAGERS % 64 == 0, "whole waves stage");
-  static_assert(BR % (2 * VG) == 0, "row pairs cover the tile");
+  static_assert((TS * 2) % 64 == 32, "pitch for transposing reads");
 };
 
-// One thread's share of staging a tile: rows kr, kr+1 of chunk dc, with the
-// row group fastest across lanes (VG lanes hold different row pairs of one
-// chunk), loaded with buffer loads (zeros past the end) and written to LDS in
-// row layout, transposed layout, or both. Threads past STAGERS, and chunks
-// past the data (d = 96), do nothing.
+// One thread's share of staging a tile: rows kr, kr+1 of chunk dc, the chunk
+// fastest across lanes (coalesced loads, contiguous LDS writes), loaded with
+// buffer loads (zeros past the end) and written to either copy. Threads past
+// STAGERS, and chunks past the data (d = 96), do nothing.
 template <int D, int BR>
 struct Stager {
   using G = Rows<D, BR>;
   bool active;       // this thread stages a chunk that holds data
   uint32_t goff;     // byte offset of row kr, chunk dc, within a tile
-  uint32_t row_wr;   // LDS byte offset, row layout
-  uint32_t t_wr[8];  // LDS byte offsets, transposed layout, per column of the chunk
-  uint32_t sel_even, sel_odd;
+  uint32_t row_wr;   // LDS byte offset, copy for row reads
+  uint32_t tr_wr;    // LDS byte offset, copy for transposing reads
 
   __device__ __forceinline__ explicit Stager(int tid) {
-    const int kr = 2 * (tid % G::VG) + 2 * G::VG * (tid / (G::VG * G::CPR));
-    const int dc = (tid / G::VG) % G::CPR;
+    const int kr = 2 * (tid / G::CPR);
+    const int dc = tid % G::CPR;
     active = (G::STAGERS == kThreads || tid < G::STAGERS) &&
              (G::CPR_DATA == G::CPR || dc < G::CPR_DATA);
     goff = (uint32_t)(kr * D + 8 * dc) * 2;
     row_wr = (uint32_t)(kr * G::KS + 8 * dc) * 2;
-    const int pos = 16 * (kr >> 4) + slice_pos(kr & 15);
-    // With 64-byte transposed rows (BR = 32), alternate lane groups write the
-    // chunk's columns in the order e ^ 1: neighbouring groups then write rows
-    // of opposite parity, on other banks (the forward's staging measured bank
-    // conflicts on these writes without it, none with it).
-    const int flip = BR == 32 ? (tid / G::VG) & 1 : 0;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int d = 8 * dc + (e ^ flip);
-      t_wr[e] = (uint32_t)(d * BR + ((pos >> 3) ^ vt_swz<BR>(d)) * 8 + (pos & 7)) * 2;
-    }
-    // v_perm selectors for the 16-bit element at an even or odd column of a
-    // 32-bit word, swapped for the flipped lane groups.
-    sel_even = flip ? 0x07060302u : 0x05040100u;
-    sel_odd = flip ? 0x05040100u : 0x07060302u;
+    tr_wr = (uint32_t)(kr * G::TS + 8 * dc) * 2;
   }
   __device__ __forceinline__ void load(rsrc_t r, int row0, u32x4 (&st)[2]) const {
     if (!active) return;
@@ -134,13 +122,32 @@ struct Stager {
                                               const u32x4 (&st)[2]) const {
     if (!active) return;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t sel = (e & 1) ? sel_odd : sel_even;
-      *reinterpret_cast<uint32_t*>(lds + base + t_wr[e]) =
-          __builtin_amdgcn_perm(st[1][e >> 1], st[0][e >> 1], sel);
-    }
+    for (int i = 0; i < 2; ++i)
+      *reinterpret_cast<u32x4*>(lds + base + tr_wr + i * G::TS * 2) = st[i];
   }
 };
+
+// Byte offset, within a copy for transposing reads, of this lane's address
+// for the A operand of a 16-row slice: lane 16 g + s points at row
+// 4 (g / 2) + s / 4, columns 16 (g % 2) + 4 (s % 4) .. +3, and then holds
+// column lane % 32 of rows 4 h .. 4 h + 3 of the slice (h = lane / 32); a
+// second read 8 rows further gives rows 8 + 4 h .. 8 + 4 h + 3. Those are the
+// rows that the B operand's slots 0-7 carry (slice_pos order).
+template <int TS>
+__device__ __forceinline__ uint32_t tr_lane_off(int lane) {
+  return (uint32_t)((4 * (lane >> 5) + ((lane & 15) >> 2)) * TS + 16 * ((lane >> 4) & 1) +
+                    4 * (lane & 3)) * 2;
+}
+
+// The 8-element A operand of rows `row0` .. row0 + 15 (a 16-row slice) and
+// columns `col0` .. col0 + 31 from a copy for transposing reads at `tile`.
+template <typename V8, int TS>
+__device__ __forceinline__ V8 tr_operand(const char* tile, uint32_t lane_off, int row0,
+                                         int col0) {
+  const char* p = tile + lane_off + (row0 * TS + col0) * 2;
+  const u32x2 lo = lds_read_tr16(p), hi = lds_read_tr16(p + 8 * TS * 2);
+  return __builtin_bit_cast(V8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+}
 
 // 2^(s*c - l2), the weight of a score s given the row's lse in log2 units.
 __device__ __forceinline__ float weight(float s, float c, float l2) {
@@ -164,7 +171,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(
   constexpr int BN = kTileRows<D>;
   using G = Rows<D, BN>;
   constexpr int KS = G::KS, NKB = BN / 32;
-  // Stage: K rows | V rows | K^T.
+  // Stage: K rows | V rows | K for transposing reads.
   constexpr int V_OFF = G::ROW * 2, KT_OFF = 2 * G::ROW * 2;
   constexpr int STAGE = (2 * G::ROW + G::TR) * 2;
   typedef typename Elem<E>::v8 v8;
@@ -232,10 +239,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(
     stg.store_trans(lds, base + KT_OFF, kst);
   };
   const uint32_t r_rd = (uint32_t)(col * KS + 8 * half) * 2;
-  uint32_t t_rd[BN / 16];
-#pragma unroll
-  for (int g = 0; g < BN / 16; ++g)
-    t_rd[g] = KT_OFF + (uint32_t)(col * BN + ((2 * g + half) ^ vt_swz<BN>(col)) * 8) * 2;
+  const uint32_t t_rd = tr_lane_off<G::TS>(lane);
 
   f32x16 acc[D / 32];
 #pragma unroll
@@ -289,8 +293,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(
         for (int sg = 0; sg < 2; ++sg)
 #pragma unroll
           for (int db = 0; db < D / 32; ++db) {
-            const v8 a = *reinterpret_cast<const v8*>(lds + base + t_rd[2 * kb + sg] +
-                                                      32 * db * BN * 2);
+            const v8 a = tr_operand<v8, G::TS>(lds + base + KT_OFF, t_rd, 32 * kb + 16 * sg,
+                                               32 * db);
             acc[db] = Elem<E>::mfma(a, dsb[kb][sg], acc[db]);
           }
     }
@@ -335,7 +339,8 @@ template <int D>
 constexpr bool kOnePass = D <= 96;
 
 // LDS stage of the key-side kernel for part P: only the tiles P reads.
-//   Q rows (S = Q K^T) | dO rows (dP) | Q^T (dK) | dO^T (dV) | lse | D (dS)
+//   Q rows (S = Q K^T) | dO rows (dP) | Q for transposing reads (dK) |
+//   dO for transposing reads (dV) | lse | D (dS)
 template <int D, int P>
 struct KeyStage {
   using G = Rows<D, kTileRows<D>>;
@@ -439,10 +444,7 @@ __global__ __launch_bounds__(kThreads, P == kDV ? 3 : 2) void attn_bwd_kv_kernel
     }
   };
   const uint32_t r_rd = (uint32_t)(col * KS + 8 * half) * 2;
-  uint32_t t_rd[BQ / 16];
-#pragma unroll
-  for (int g = 0; g < BQ / 16; ++g)
-    t_rd[g] = (uint32_t)(col * BQ + ((2 * g + half) ^ vt_swz<BQ>(col)) * 8) * 2;
+  const uint32_t t_rd = tr_lane_off<G::TS>(lane);
 
   f32x16 dkacc[kWantDK ? D / 32 : 1], dvacc[kWantDV ? D / 32 : 1];
 #pragma unroll
@@ -503,13 +505,14 @@ __global__ __launch_bounds__(kThreads, P == kDV ? 3 : 2) void attn_bwd_kv_kernel
         for (int sg = 0; sg < 2; ++sg)
 #pragma unroll
           for (int db = 0; db < D / 32; ++db) {
-            const uint32_t at = base + t_rd[2 * qb + sg] + 32 * db * BQ * 2;
             if constexpr (kWantDV)
-              dvacc[db] = Elem<E>::mfma(*reinterpret_cast<const v8*>(lds + at + S_::DOT_OFF),
-                                        pb[qb][sg], dvacc[db]);
+              dvacc[db] = Elem<E>::mfma(
+                  tr_operand<v8, G::TS>(lds + base + S_::DOT_OFF, t_rd, 32 * qb + 16 * sg, 32 * db),
+                  pb[qb][sg], dvacc[db]);
             if constexpr (kWantDK)
-              dkacc[db] = Elem<E>::mfma(*reinterpret_cast<const v8*>(lds + at + S_::QT_OFF),
-                                        dsb[qb][sg], dkacc[db]);
+              dkacc[db] = Elem<E>::mfma(
+                  tr_operand<v8, G::TS>(lds + base + S_::QT_OFF, t_rd, 32 * qb + 16 * sg, 32 * db),
+                  dsb[qb][sg], dkacc[db]);
           }
     }
 
