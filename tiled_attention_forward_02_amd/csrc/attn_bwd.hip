@@ -64,25 +64,22 @@ template <int D>
 constexpr int kLayoutD = D == 96 ? 128 : D;
 
 // A tile of BR rows of a [*, D] tensor in LDS, in up to two row-major
-// copies: pitch DL + 8 for 16-byte row reads (the 16-byte pad spreads the
-// rows read by 8 lanes over distinct bank groups), and pitch DL + 16 for
-// transposing reads (an odd multiple of 32 bytes: the 4 rows x 32 bytes a
-// 16-lane group reads fall in distinct 32-byte slots of a 128-byte bank
-// row). A staging thread moves two rows of one 16-byte chunk; at d = 32 half
-// the threads do.
+// copies: pitch DL + 8 for 16-byte row reads (the 16-byte pad puts the 16
+// rows one read pass touches on distinct banks), and tr_pitch for
+// transposing reads. A staging thread moves two rows of one 16-byte chunk;
+// at d = 32 half the threads do.
 template <int D, int BR_>
 struct Rows {
   static constexpr int DL = kLayoutD<D>;
   static constexpr int BR = BR_;
   static constexpr int KS = DL + 8;
-  static constexpr int TS = DL + 16;
+  static constexpr int TS = tr_pitch<DL>();
   static constexpr int ROW = BR * KS;  // elements, copy for row reads
   static constexpr int TR = BR * TS;   // elements, copy for transposing reads
   static constexpr int CPR = DL / 8;   // 16-byte chunks per row of the layout
   static constexpr int CPR_DATA = D / 8;  // chunks that hold data
   static constexpr int STAGERS = BR * CPR / 2;  // threads that stage a tile
   static_assert(STAGERS <= kThreads && STAGERS % 64 == 0, "whole waves stage");
-  static_assert((TS * 2) % 64 == 32, "pitch for transposing reads");
 };
 
 // One thread's share of staging a tile: rows kr, kr+1 of chunk dc, the chunk

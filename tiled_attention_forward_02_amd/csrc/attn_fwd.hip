@@ -113,10 +113,7 @@ struct Tile {
   static constexpr int NKB = BN / 32;            // 32-key MFMA blocks per tile
   static constexpr int KS = D + 8;               // K row pitch in LDS (bf16), 16 B pad
   static constexpr int K_ELEMS = BN * KS;        // one K tile
-  // V row pitch in LDS (elements): an odd multiple of 32 bytes, so the
-  // 4 consecutive rows x 32 bytes that a 16-lane group of a transposing read
-  // touches fall in distinct 32-byte slots of a 128-byte bank row.
-  static constexpr int VS = D + 16;
+  static constexpr int VS = tr_pitch<D>();       // V row pitch in LDS
   static constexpr int V_ELEMS = BN * VS;        // one V tile, row-major
   static constexpr int CPR = D / 8;              // 16-byte chunks per row
   static constexpr int KPT = BN * CPR / kThreads;  // rows each thread stages (4 or 2)
@@ -124,7 +121,6 @@ struct Tile {
   static constexpr int LDS_ELEMS = 2 * STAGE;
   static constexpr int LDS_BYTES = 2 * LDS_ELEMS;
   static_assert(KPT == 2 || KPT == 4, "staging layout");
-  static_assert((VS * 2) % 64 == 32, "V pitch");
 };
 
 template <typename E, int D, bool CAUSAL>

@@ -119,6 +119,17 @@ __device__ __forceinline__ void load16_lds(rsrc_t r, char* lds_base, uint32_t by
       r, (__attribute__((address_space(3))) void*)lds_base, 16, (int)byte_off, 0, 0, 0);
 }
 
+// Row pitch (elements) of a row-major tile read by lds_read_tr16, for layout
+// head dimension DL. The 64-bank LDS serves 32 lanes of an 8-byte read at a
+// time; those lanes cover 4 consecutive rows x 64 bytes, conflict-free when
+// the rows start an odd multiple of 64 bytes apart (VS = 32 mod 64). At
+// DL = 64 that pitch (96) would keep four workgroups from fitting in LDS, so
+// it stays at 80 (those reads take two passes).
+template <int DL>
+constexpr int tr_pitch() {
+  return DL == 64 ? 80 : (DL % 64 == 32 ? DL : DL + 32);
+}
+
 // Transposing LDS read of 16-bit data (ds_read_b64_tr_b16). Each lane gives
 // the address of 4 consecutive elements (8 bytes). Within each group of 16
 // lanes, lane 4a + b receives, as its element e, element b of the 4 given by
