@@ -310,14 +310,31 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : D >= 96 ? 3 : 2) void attn
 
       if constexpr (kMfmaPriority<D>) __builtin_amdgcn_s_setprio(0);
       // Keys past the end and (causal) keys after the query get -inf.
+      // Register i of block kb holds key k0 + 4 half + o_i. Up to 32 scores
+      // a lane, a compare and select per score; past that (d = 32) the
+      // compares' lane masks overflow the SGPRs and spill, so a bit select
+      // on the sign of lim - o_i, lim being the last key the lane's query
+      // sees less k0 + 4 half. (The bit select costs VGPRs elsewhere: at
+      // d = 96 it would cost the fourth wave per SIMD.)
       if ((k0 + BN > Nk) || (CAUSAL && k0 + BN - 1 > qw + off)) {
+        if constexpr (NKB * 16 > 32) {
+          const int lim = (CAUSAL ? min(Nk - 1, qi + off) : Nk - 1) - k0 - 4 * half;
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
+          for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = k0 + 32 * kb + 8 * (i >> 2) + 4 * half + (i & 3);
-            if (key >= Nk || (CAUSAL && key > qi + off)) sacc[kb][i] = -INFINITY;
-          }
+            for (int i = 0; i < 16; ++i) {
+              const int o = 32 * kb + 8 * (i >> 2) + (i & 3);
+              sacc[kb][i] = neg_inf_where((lim - o) >> 31, sacc[kb][i]);
+            }
+        } else {
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int key = k0 + 32 * kb + 8 * (i >> 2) + 4 * half + (i & 3);
+              if (key >= Nk || (CAUSAL && key > qi + off)) sacc[kb][i] = -INFINITY;
+            }
+        }
       }
 
       // P = 2^(s*c - m_run), rounded to bf16, and its row sum (fp32).

@@ -13,6 +13,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <math.h>
 #include <stdint.h>
 
 namespace mi_attn {
@@ -139,6 +140,16 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const char* p) {
   const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (__attribute__((address_space(3))) s16x4*)(p));
   return __builtin_bit_cast(u32x2, r);
+}
+
+// -inf where `masked` has all bits set, x where it is 0: one v_bfi_b32. A
+// bit select on a sign-extended difference needs no per-element lane mask
+// (a compare would hold one SGPR pair per element of a tile until its
+// select, more than the SGPR file at 64 elements).
+__device__ __forceinline__ float neg_inf_where(int masked, float x) {
+  float r;
+  asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "v"(masked), "s"(-INFINITY), "v"(x));
+  return r;
 }
 
 // Value of x in the lane 32 positions away, combined with op (same result in
