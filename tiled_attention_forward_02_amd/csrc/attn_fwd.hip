@@ -113,11 +113,14 @@ struct Tile {
   static constexpr int NKB = BN / 32;            // 32-key MFMA blocks per tile
   static constexpr int KS = D + 8;               // K row pitch in LDS (bf16), 16 B pad
   static constexpr int K_ELEMS = BN * KS;        // one K tile
+  // LDS span of a K tile: rounded up to 1024 bytes, so that DMA instructions
+  // (1024 bytes each) that run past the tile write its padding, not V.
+  static constexpr int K_SPAN = (K_ELEMS + 511) / 512 * 512;
   static constexpr int VS = tr_pitch<D>();       // V row pitch in LDS
   static constexpr int V_ELEMS = BN * VS;        // one V tile, row-major
   static constexpr int CPR = D / 8;              // 16-byte chunks per row
   static constexpr int KPT = BN * CPR / kThreads;  // rows each thread stages (4 or 2)
-  static constexpr int STAGE = K_ELEMS + V_ELEMS;
+  static constexpr int STAGE = K_SPAN + V_ELEMS;
   static constexpr int LDS_ELEMS = 2 * STAGE;
   static constexpr int LDS_BYTES = 2 * LDS_ELEMS;
   static_assert(KPT == 2 || KPT == 4, "staging layout");
@@ -134,10 +137,13 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : D >= 96 ? 3 : 2) void attn
   constexpr int CPR_DATA = D / 8;
   typedef typename Elem<E>::v8 v8;
   typedef typename Elem<E>::v4 v4;
-  __shared__ __attribute__((aligned(16))) E smem[T::LDS_ELEMS];
+  __shared__ __attribute__((aligned(1024))) E smem[T::LDS_ELEMS];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, col = lane & 31, half = lane >> 5;
+  // The wave index is uniform across the wave; readfirstlane lets the
+  // compiler keep it (and what follows from it) in scalar registers.
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, col = lane & 31, half = lane >> 5;
 
   int bh, qt;
   map_block(blockIdx.x, BH, nq, CAUSAL, bh, qt);
@@ -189,46 +195,43 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : D >= 96 ? 3 : 2) void attn
   // registers). A tile in LDS is BN rows of row_slots 16-byte slots (the
   // row's data chunks, then its pad); one wave instruction writes 64
   // consecutive slots at its LDS base, lane l the slot 64 u + l of
-  // instruction u. Each lane's (row, chunk) for its slots is fixed; pad slots
-  // and chunks past the data (d = 96) are masked off. The tile's first key
-  // goes into the vector offset, so the buffer range check still zero-fills
-  // rows past Nk.
+  // instruction u (u = wave, wave + 4, ...; whether u is in the tile is a
+  // uniform branch). Lanes of pad slots, of chunks past the data (d = 96)
+  // and past the tile get an offset beyond any buffer, which the range check
+  // turns into zeros without a fetch, so no lane is masked: the last
+  // instruction of a K tile writes its padding. The tile's first key goes
+  // into the vector offset, so the range check still zero-fills rows past
+  // Nk.
+  constexpr uint32_t kNoFetch = 0x80000000u;  // + k0 * D * 2 < 2^31: no wrap
   constexpr int KROW_SLOTS = KS / 8, VROW_SLOTS = T::VS / 8;
   constexpr int KINSTR = (BN * KROW_SLOTS + 63) / 64;      // per tile
   constexpr int VINSTR = (BN * VROW_SLOTS + 63) / 64;
-  constexpr int KI_W = (KINSTR + kWaves - 1) / kWaves;     // per wave, at most
+  constexpr int KI_W = (KINSTR + kWaves - 1) / kWaves;     // per wave
   constexpr int VI_W = (VINSTR + kWaves - 1) / kWaves;
+  static_assert(KINSTR * 512 <= T::K_SPAN, "K DMA stays within the K span");
+  static_assert(!kVDma<D> || VINSTR * 512 == T::V_ELEMS, "V DMA covers the V tile exactly");
+  lds_char* const lds3 = to_lds(smem);
+  auto dma_off = [&](int u, int row_slots) {
+    const int slot = 64 * u + lane, row = slot / row_slots, ch = slot % row_slots;
+    return row < BN && ch < CPR_DATA ? (uint32_t)(row * D + 8 * ch) * 2 : kNoFetch;
+  };
   uint32_t kdma_off[KI_W], vdma_off[VI_W];
-  bool kdma_on[KI_W], vdma_on[VI_W];
 #pragma unroll
-  for (int i = 0; i < KI_W; ++i) {
-    const int u = wave + kWaves * i, slot = 64 * u + lane;
-    const int row = slot / KROW_SLOTS, ch = slot % KROW_SLOTS;
-    kdma_on[i] = u < KINSTR && slot < BN * KROW_SLOTS && ch < CPR_DATA;
-    kdma_off[i] = (uint32_t)(row * D + 8 * ch) * 2;
-  }
+  for (int i = 0; i < KI_W; ++i) kdma_off[i] = dma_off(wave + kWaves * i, KROW_SLOTS);
 #pragma unroll
-  for (int i = 0; i < VI_W; ++i) {
-    const int u = wave + kWaves * i, slot = 64 * u + lane;
-    const int row = slot / VROW_SLOTS, ch = slot % VROW_SLOTS;
-    vdma_on[i] = u < VINSTR && slot < BN * VROW_SLOTS && ch < CPR_DATA;
-    vdma_off[i] = (uint32_t)(row * D + 8 * ch) * 2;
-  }
+  for (int i = 0; i < VI_W; ++i) vdma_off[i] = dma_off(wave + kWaves * i, VROW_SLOTS);
+  auto dma_tile = [&](rsrc_t r, uint32_t tile, const uint32_t* offs, int ninstr, int nw, int k0)
+      __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < nw; ++i) {
+      const int u = wave + kWaves * i;
+      if (u < ninstr) load16_lds(r, lds3 + tile + 1024 * u, offs[i] + (uint32_t)k0 * D * 2);
+    }
+  };
   auto dma = [&](auto stage_c, int k0) {
     constexpr uint32_t base = decltype(stage_c)::value * T::STAGE * 2;
-    if constexpr (kKDma<D>) {
-#pragma unroll
-      for (int i = 0; i < KI_W; ++i)
-        if (wave + kWaves * i < KINSTR && kdma_on[i])
-          load16_lds(rk, lds + base + 1024 * (wave + kWaves * i), kdma_off[i] + (uint32_t)k0 * D * 2);
-    }
-    if constexpr (kVDma<D>) {
-#pragma unroll
-      for (int i = 0; i < VI_W; ++i)
-        if (wave + kWaves * i < VINSTR && vdma_on[i])
-          load16_lds(rv, lds + base + T::K_ELEMS * 2 + 1024 * (wave + kWaves * i),
-                     vdma_off[i] + (uint32_t)k0 * D * 2);
-    }
+    if constexpr (kKDma<D>) dma_tile(rk, base, kdma_off, KINSTR, KI_W, k0);
+    if constexpr (kVDma<D>) dma_tile(rv, base + T::K_SPAN * 2, vdma_off, VINSTR, VI_W, k0);
   };
 
   // Staging through registers: thread owns rows kr .. kr+KPT-1 and 16-byte
@@ -255,14 +258,14 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : D >= 96 ? 3 : 2) void attn
   };
   // Per-lane LDS byte offsets that do not change with the tile.
   const uint32_t k_wr = (uint32_t)(kr * KS + 8 * dc) * 2;
-  const uint32_t v_wr = (uint32_t)(T::K_ELEMS + kr * T::VS + 8 * dc) * 2;
+  const uint32_t v_wr = (uint32_t)(T::K_SPAN + kr * T::VS + 8 * dc) * 2;
   const uint32_t k_rd = (uint32_t)(col * KS + 8 * half) * 2;
   // V^T fragment of a 16-key slice and 32 columns: two transposing reads, 8
   // keys apart. Lane 16 g + s points at row 4 (g / 2) + s / 4, columns
   // 16 (g % 2) + 4 (s % 4) .. +3 of the slice; it then holds column
   // col of keys 4 half .. 4 half + 3 (and 8 further with the second read),
   // the keys its P^T register slots carry (see slice_pos).
-  const uint32_t v_rd = (uint32_t)(T::K_ELEMS + (4 * half + ((lane & 15) >> 2)) * T::VS +
+  const uint32_t v_rd = (uint32_t)(T::K_SPAN + (4 * half + ((lane & 15) >> 2)) * T::VS +
                                    16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
 
   auto lds_store = [&](auto stage_c) {

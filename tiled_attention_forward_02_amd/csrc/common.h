@@ -111,11 +111,18 @@ __device__ __forceinline__ u32x4 load16(rsrc_t r, uint32_t byte_off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 0);
 }
 
+// A byte in LDS, addressed as such (a generic pointer cast to LDS needs a
+// null check at each use).
+typedef __attribute__((address_space(3))) char lds_char;
+__device__ __forceinline__ lds_char* to_lds(void* shared_array) {
+  return (lds_char*)shared_array;
+}
+
 // 16 bytes per lane from the buffer at byte_off straight into LDS, no
 // registers: the wave's 64 lanes fill the 1024 bytes at lds_base in lane
-// order (lane l at lds_base + 16 l). The range check applies as for load16.
-// Completion is counted by vmcnt, like any buffer load.
-__device__ __forceinline__ void load16_lds(rsrc_t r, char* lds_base, uint32_t byte_off) {
+// order (lane l at lds_base + 16 l); an offset past the buffer writes zeros
+// without a fetch. Completion is counted by vmcnt, like any buffer load.
+__device__ __forceinline__ void load16_lds(rsrc_t r, lds_char* lds_base, uint32_t byte_off) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(
       r, (__attribute__((address_space(3))) void*)lds_base, 16, (int)byte_off, 0, 0, 0);
 }
