@@ -66,62 +66,19 @@ constexpr int kLayoutD = D == 96 ? 128 : D;
 // A tile of BR rows of a [*, D] tensor in LDS, in up to two row-major
 // copies: pitch DL + 8 for 16-byte row reads (the 16-byte pad puts the 16
 // rows one read pass touches on distinct banks), and tr_pitch for
-// transposing reads. A staging thread moves two rows of one 16-byte chunk;
-// at d = 32 half the threads do.
+// transposing reads. Each copy is loaded by LDS DMA (DmaTile) straight from
+// the tensor and takes a multiple of 1024 bytes of LDS (its DMA span).
 template <int D, int BR_>
 struct Rows {
   static constexpr int DL = kLayoutD<D>;
   static constexpr int BR = BR_;
   static constexpr int KS = DL + 8;
   static constexpr int TS = tr_pitch<DL>();
-  static constexpr int ROW = BR * KS;  // elements, copy for row reads
-  static constexpr int TR = BR * TS;   // elements, copy for transposing reads
-  static constexpr int CPR = DL / 8;   // 16-byte chunks per row of the layout
-  static constexpr int CPR_DATA = D / 8;  // chunks that hold data
-  static constexpr int STAGERS = BR * CPR / 2;  // threads that stage a tile
-  static_assert(STAGERS <= kThreads && STAGERS % 64 == 0, "whole waves stage");
-};
-
-// One thread's share of staging a tile: rows kr, kr+1 of chunk dc, the chunk
-// fastest across lanes (coalesced loads, contiguous LDS writes), loaded with
-// buffer loads (zeros past the end) and written to either copy. Threads past
-// STAGERS, and chunks past the data (d = 96), do nothing.
-template <int D, int BR>
-struct Stager {
-  using G = Rows<D, BR>;
-  bool active;       // this thread stages a chunk that holds data
-  uint32_t goff;     // byte offset of row kr, chunk dc, within a tile
-  uint32_t row_wr;   // LDS byte offset, copy for row reads
-  uint32_t tr_wr;    // LDS byte offset, copy for transposing reads
-
-  __device__ __forceinline__ explicit Stager(int tid) {
-    const int kr = 2 * (tid / G::CPR);
-    const int dc = tid % G::CPR;
-    active = (G::STAGERS == kThreads || tid < G::STAGERS) &&
-             (G::CPR_DATA == G::CPR || dc < G::CPR_DATA);
-    goff = (uint32_t)(kr * D + 8 * dc) * 2;
-    row_wr = (uint32_t)(kr * G::KS + 8 * dc) * 2;
-    tr_wr = (uint32_t)(kr * G::TS + 8 * dc) * 2;
-  }
-  __device__ __forceinline__ void load(rsrc_t r, int row0, u32x4 (&st)[2]) const {
-    if (!active) return;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) st[i] = load16(r, goff + (uint32_t)((row0 + i) * D * 2));
-  }
-  __device__ __forceinline__ void store_rows(char* lds, uint32_t base,
-                                             const u32x4 (&st)[2]) const {
-    if (!active) return;
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-      *reinterpret_cast<u32x4*>(lds + base + row_wr + i * G::KS * 2) = st[i];
-  }
-  __device__ __forceinline__ void store_trans(char* lds, uint32_t base,
-                                              const u32x4 (&st)[2]) const {
-    if (!active) return;
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-      *reinterpret_cast<u32x4*>(lds + base + tr_wr + i * G::TS * 2) = st[i];
-  }
+  typedef DmaTile<D, BR, KS> RowDma;
+  typedef DmaTile<D, BR, TS> TrDma;
+  static constexpr int ROW_SPAN = RowDma::SPAN;  // bytes, copy for row reads
+  static constexpr int TR_SPAN = TrDma::SPAN;    // bytes, copy for transposing reads
+  static_assert(ROW_SPAN >= BR * KS * 2 && TR_SPAN >= BR * TS * 2, "DMA spans hold the tiles");
 };
 
 // Byte offset, within a copy for transposing reads, of this lane's address
@@ -169,14 +126,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(
   using G = Rows<D, BN>;
   constexpr int KS = G::KS, NKB = BN / 32;
   // Stage: K rows | V rows | K for transposing reads.
-  constexpr int V_OFF = G::ROW * 2, KT_OFF = 2 * G::ROW * 2;
-  constexpr int STAGE = (2 * G::ROW + G::TR) * 2;
+  constexpr int V_OFF = G::ROW_SPAN, KT_OFF = 2 * G::ROW_SPAN;
+  constexpr int STAGE = 2 * G::ROW_SPAN + G::TR_SPAN;
   typedef typename Elem<E>::v8 v8;
   typedef typename Elem<E>::v4 v4;
-  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, col = lane & 31, half = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar registers
+  const int lane = tid & 63, col = lane & 31, half = lane >> 5;
   int bh, qt;
   map_block(blockIdx.x, BH, nq, CAUSAL, bh, qt);
   const int q0 = qt * kBlockRows;
@@ -222,18 +180,17 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(
   const int nt = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
   const int wave_kv_end = CAUSAL ? min(Nk, qw + 32 + off) : Nk;
 
-  const Stager<D, BN> stg(tid);
-  u32x4 kst[2], vst[2];
-  auto gload = [&](int k0) __attribute__((always_inline)) {
-    stg.load(rk, k0, kst);
-    stg.load(rv, k0, vst);
-  };
+  // The key tile from k0 into a stage, by DMA (K twice: rows and the copy
+  // for transposing reads).
+  const typename G::RowDma row_dma(wave, lane);
+  const typename G::TrDma tr_dma(wave, lane);
   char* const lds = smem;
-  auto lds_store = [&](auto stage_c) __attribute__((always_inline)) {
+  lds_char* const lds3 = to_lds(smem);
+  auto stage_tile = [&](auto stage_c, int k0) __attribute__((always_inline)) {
     constexpr uint32_t base = decltype(stage_c)::value * STAGE;
-    stg.store_rows(lds, base, kst);
-    stg.store_rows(lds, base + V_OFF, vst);
-    stg.store_trans(lds, base + KT_OFF, kst);
+    row_dma.issue(rk, lds3 + base, wave, k0);
+    row_dma.issue(rv, lds3 + base + V_OFF, wave, k0);
+    tr_dma.issue(rk, lds3 + base + KT_OFF, wave, k0);
   };
   const uint32_t r_rd = (uint32_t)(col * KS + 8 * half) * 2;
   const uint32_t t_rd = tr_lane_off<G::TS>(lane);
@@ -246,7 +203,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(
     constexpr uint32_t base = decltype(stage_c)::value * STAGE;
     const int k0 = t * BN;
     const bool has_next = t + 1 < nt;
-    if (has_next) gload(k0 + BN);
+    if (has_next) stage_tile(std::integral_constant<int, decltype(stage_c)::value ^ 1>{}, k0 + BN);
 
     if (k0 < wave_kv_end) {
       // S^T = K Q^T and dP^T = V dO^T, 32 keys per accumulator.
@@ -296,13 +253,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(
           }
     }
 
-    if (has_next) lds_store(std::integral_constant<int, decltype(stage_c)::value ^ 1>{});
+    // The next tile lands in LDS with no instruction of this wave writing it:
+    // wait for its loads before the barrier.
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
 
   if (nt > 0) {
-    gload(0);
-    lds_store(std::integral_constant<int, 0>{});
+    stage_tile(std::integral_constant<int, 0>{}, 0);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
   for (int t = 0; t < nt; t += 2) {
@@ -346,10 +305,10 @@ struct KeyStage {
   static constexpr bool kQT = P != kDV;
   static constexpr bool kDOT = P != kDK;
   static constexpr bool kDelta = P != kDV;
-  static constexpr int DO_OFF = G::ROW * 2;
-  static constexpr int QT_OFF = DO_OFF + (kDORows ? G::ROW * 2 : 0);
-  static constexpr int DOT_OFF = QT_OFF + (kQT ? G::TR * 2 : 0);
-  static constexpr int L_OFF = DOT_OFF + (kDOT ? G::TR * 2 : 0);
+  static constexpr int DO_OFF = G::ROW_SPAN;
+  static constexpr int QT_OFF = DO_OFF + (kDORows ? G::ROW_SPAN : 0);
+  static constexpr int DOT_OFF = QT_OFF + (kQT ? G::TR_SPAN : 0);
+  static constexpr int L_OFF = DOT_OFF + (kDOT ? G::TR_SPAN : 0);
   static constexpr int D_OFF = L_OFF + BQ * 4;
   static constexpr int BYTES = D_OFF + (kDelta ? BQ * 4 : 0);
   static_assert(BYTES % 16 == 0 && L_OFF % 16 == 0, "16-byte aligned LDS tiles");
@@ -369,10 +328,11 @@ __global__ __launch_bounds__(kThreads, P == kDV ? 3 : 2) void attn_bwd_kv_kernel
   constexpr int STAGE = S_::BYTES;
   typedef typename Elem<E>::v8 v8;
   typedef typename Elem<E>::v4 v4;
-  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, col = lane & 31, half = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar registers
+  const int lane = tid & 63, col = lane & 31, half = lane >> 5;
   int bh, kt;
   map_block(blockIdx.x, BH, nk, CAUSAL, bh, kt);
   // Causal: key tile 0 sees the most queries; map_block deals the last index
@@ -410,16 +370,22 @@ __global__ __launch_bounds__(kThreads, P == kDV ? 3 : 2) void attn_bwd_kv_kernel
   const int qt0 = q_begin / BQ;
   const int nt = q_begin < Nq ? (Nq + BQ - 1) / BQ - qt0 : 0;
 
-  const Stager<D, BQ> stg(tid);
-  u32x4 qst[2], dst[2];
-  // lse and D of the next tile's rows (threads tid < BQ), kept raw until the
-  // tile is written to LDS: using them at once would wait for every load in
-  // flight, the tile's own included.
+  // The query tile from q0 into a stage, by DMA; its lse and D (threads
+  // tid < BQ) through registers, kept raw until written to LDS at the end of
+  // the step: using them at once would wait for every load in flight, the
+  // tile's own included.
+  const typename G::RowDma row_dma(wave, lane);
+  const typename G::TrDma tr_dma(wave, lane);
+  char* const lds = smem;
+  lds_char* const lds3 = to_lds(smem);
   uint32_t lraw = 0, draw = 0;
   bool lvalid = false;
-  auto gload = [&](int q0) __attribute__((always_inline)) {
-    stg.load(rq, q0, qst);
-    stg.load(rdo, q0, dst);
+  auto gload = [&](auto stage_c, int q0) __attribute__((always_inline)) {
+    constexpr uint32_t base = decltype(stage_c)::value * STAGE;
+    row_dma.issue(rq, lds3 + base, wave, q0);
+    if constexpr (S_::kDORows) row_dma.issue(rdo, lds3 + base + S_::DO_OFF, wave, q0);
+    if constexpr (S_::kQT) tr_dma.issue(rq, lds3 + base + S_::QT_OFF, wave, q0);
+    if constexpr (S_::kDOT) tr_dma.issue(rdo, lds3 + base + S_::DOT_OFF, wave, q0);
     if (tid < BQ) {
       const int qrow = q0 + tid;
       lvalid = qrow < Nq;
@@ -427,13 +393,8 @@ __global__ __launch_bounds__(kThreads, P == kDV ? 3 : 2) void attn_bwd_kv_kernel
       if constexpr (S_::kDelta) draw = __builtin_amdgcn_raw_buffer_load_b32(rd, qrow * 4, 0, 0);
     }
   };
-  char* const lds = smem;
   auto lds_store = [&](auto stage_c) __attribute__((always_inline)) {
     constexpr uint32_t base = decltype(stage_c)::value * STAGE;
-    stg.store_rows(lds, base, qst);
-    if constexpr (S_::kDORows) stg.store_rows(lds, base + S_::DO_OFF, dst);
-    if constexpr (S_::kQT) stg.store_trans(lds, base + S_::QT_OFF, qst);
-    if constexpr (S_::kDOT) stg.store_trans(lds, base + S_::DOT_OFF, dst);
     if (tid < BQ) {
       *reinterpret_cast<float*>(lds + base + S_::L_OFF + tid * 4) =
           lse_log2(__uint_as_float(lraw), lvalid);
@@ -454,7 +415,7 @@ __global__ __launch_bounds__(kThreads, P == kDV ? 3 : 2) void attn_bwd_kv_kernel
     constexpr uint32_t base = decltype(stage_c)::value * STAGE;
     const int q0 = (qt0 + t) * BQ;
     const bool has_next = t + 1 < nt;
-    if (has_next) gload(q0 + BQ);
+    if (has_next) gload(std::integral_constant<int, decltype(stage_c)::value ^ 1>{}, q0 + BQ);
 
     // Some query of the tile sees a key of this wave.
     if (!CAUSAL || q0 + BQ - 1 + off >= kw) {
@@ -514,12 +475,16 @@ __global__ __launch_bounds__(kThreads, P == kDV ? 3 : 2) void attn_bwd_kv_kernel
     }
 
     if (has_next) lds_store(std::integral_constant<int, decltype(stage_c)::value ^ 1>{});
+    // The next tile lands in LDS with no instruction of this wave writing it:
+    // wait for its loads before the barrier.
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
 
   if (nt > 0) {
-    gload(qt0 * BQ);
+    gload(std::integral_constant<int, 0>{}, qt0 * BQ);
     lds_store(std::integral_constant<int, 0>{});
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
   for (int t = 0; t < nt; t += 2) {
