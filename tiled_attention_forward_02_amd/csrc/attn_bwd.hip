@@ -20,12 +20,10 @@
 //    forms D_i from its own rows of O and dO and writes it to `delta`.
 //      S^T = K Q^T,  dP^T = V dO^T,  dS^T = P^T * (dP^T - D),  dQ^T += K^T dS^T
 //  * key-side kernel: one workgroup per 128 keys (a key per lane), query
-//    tiles streamed through LDS in row and transposed layouts.
+//    tiles streamed through LDS in two row-major copies (row reads and
+//    transposing reads); one pass accumulates both gradients.
 //      S = Q K^T,  dP = dO V^T,  dS = P * (dP - D),
 //      dV^T += dO^T P,  dK^T += Q^T dS
-//    At d=64 one pass does both; at d=128 one pass does dV (S, P) and a
-//    second dK (S, dP, dS), which keeps two or three waves per SIMD instead
-//    of one.
 //
 // In both, the C accumulator of P or dS, rounded to the input type, is the B
 // operand of the next product once the rows inside each 16-row slice follow
@@ -286,45 +284,36 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(
 
 // ---------------------------------------------------------- dK/dV kernel --
 
-// Which key gradients one launch of the key-side kernel accumulates. Both at
-// once need the K and V fragments and two accumulators live (one wave per
-// SIMD at d=128); dV alone (S, P, dV) and dK alone (S, dP, dS, dK) each fit
-// two or three waves per SIMD, for one extra recomputation of S.
-enum Part { kBoth = 0, kDV = 1, kDK = 2 };
-template <int D>
-constexpr bool kOnePass = D <= 96;
+// One pass accumulates both dK and dV: the K and V fragments and the two
+// accumulators fit two waves per SIMD at every head dimension (256 VGPRs at
+// d = 128, with two values spilled outside the loop).
 
-// LDS stage of the key-side kernel for part P: only the tiles P reads.
+// LDS stage of the key-side kernel:
 //   Q rows (S = Q K^T) | dO rows (dP) | Q for transposing reads (dK) |
 //   dO for transposing reads (dV) | lse | D (dS)
-template <int D, int P>
+template <int D>
 struct KeyStage {
   using G = Rows<D, kTileRows<D>>;
   static constexpr int BQ = G::BR;
-  static constexpr bool kDORows = P != kDV;
-  static constexpr bool kQT = P != kDV;
-  static constexpr bool kDOT = P != kDK;
-  static constexpr bool kDelta = P != kDV;
   static constexpr int DO_OFF = G::ROW_SPAN;
-  static constexpr int QT_OFF = DO_OFF + (kDORows ? G::ROW_SPAN : 0);
-  static constexpr int DOT_OFF = QT_OFF + (kQT ? G::TR_SPAN : 0);
-  static constexpr int L_OFF = DOT_OFF + (kDOT ? G::TR_SPAN : 0);
+  static constexpr int QT_OFF = DO_OFF + G::ROW_SPAN;
+  static constexpr int DOT_OFF = QT_OFF + G::TR_SPAN;
+  static constexpr int L_OFF = DOT_OFF + G::TR_SPAN;
   static constexpr int D_OFF = L_OFF + BQ * 4;
-  static constexpr int BYTES = D_OFF + (kDelta ? BQ * 4 : 0);
+  static constexpr int BYTES = D_OFF + BQ * 4;
   static_assert(BYTES % 16 == 0 && L_OFF % 16 == 0, "16-byte aligned LDS tiles");
 };
 
-template <typename E, int D, bool CAUSAL, int P>
-__global__ __launch_bounds__(kThreads, P == kDV ? 3 : 2) void attn_bwd_kv_kernel(
+template <typename E, int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 2) void attn_bwd_kv_kernel(
     const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict__ V,
     const float* __restrict__ LSE, const E* __restrict__ dO, const float* __restrict__ Delta,
     E* __restrict__ dK, E* __restrict__ dV, int BH, int Nq, int Nk, int nk, float c,
     float dk_scale) {
-  using S_ = KeyStage<D, P>;
+  using S_ = KeyStage<D>;
   using G = typename S_::G;
   constexpr int BQ = S_::BQ;
   constexpr int KS = G::KS, NQB = BQ / 32;
-  constexpr bool kWantDK = P != kDV, kWantDV = P != kDK;
   constexpr int STAGE = S_::BYTES;
   typedef typename Elem<E>::v8 v8;
   typedef typename Elem<E>::v4 v4;
@@ -353,7 +342,7 @@ __global__ __launch_bounds__(kThreads, P == kDV ? 3 : 2) void attn_bwd_kv_kernel
   const rsrc_t rd = make_rsrc(Delta + (size_t)bh * Nq, (uint32_t)Nq * 4);
 
   // K^T and V^T fragments (B operands, a key per lane); zero past Nk.
-  v8 kf[D / 16], vf[kWantDK ? D / 16 : 1];
+  v8 kf[D / 16], vf[D / 16];
   {
     const rsrc_t rk = make_rsrc(K + khead, k_bytes);
     const rsrc_t rv = make_rsrc(V + khead, k_bytes);
@@ -361,7 +350,7 @@ __global__ __launch_bounds__(kThreads, P == kDV ? 3 : 2) void attn_bwd_kv_kernel
     for (int s = 0; s < D / 16; ++s) {
       const uint32_t at = (uint32_t)(kj * D + 16 * s + 8 * half) * 2;
       kf[s] = __builtin_bit_cast(v8, load16(rk, at));
-      if constexpr (kWantDK) vf[s] = __builtin_bit_cast(v8, load16(rv, at));
+      vf[s] = __builtin_bit_cast(v8, load16(rv, at));
     }
   }
 
@@ -383,14 +372,14 @@ __global__ __launch_bounds__(kThreads, P == kDV ? 3 : 2) void attn_bwd_kv_kernel
   auto gload = [&](auto stage_c, int q0) __attribute__((always_inline)) {
     constexpr uint32_t base = decltype(stage_c)::value * STAGE;
     row_dma.issue(rq, lds3 + base, wave, q0);
-    if constexpr (S_::kDORows) row_dma.issue(rdo, lds3 + base + S_::DO_OFF, wave, q0);
-    if constexpr (S_::kQT) tr_dma.issue(rq, lds3 + base + S_::QT_OFF, wave, q0);
-    if constexpr (S_::kDOT) tr_dma.issue(rdo, lds3 + base + S_::DOT_OFF, wave, q0);
+    row_dma.issue(rdo, lds3 + base + S_::DO_OFF, wave, q0);
+    tr_dma.issue(rq, lds3 + base + S_::QT_OFF, wave, q0);
+    tr_dma.issue(rdo, lds3 + base + S_::DOT_OFF, wave, q0);
     if (tid < BQ) {
       const int qrow = q0 + tid;
       lvalid = qrow < Nq;
       lraw = __builtin_amdgcn_raw_buffer_load_b32(rl, qrow * 4, 0, 0);
-      if constexpr (S_::kDelta) draw = __builtin_amdgcn_raw_buffer_load_b32(rd, qrow * 4, 0, 0);
+      draw = __builtin_amdgcn_raw_buffer_load_b32(rd, qrow * 4, 0, 0);
     }
   };
   auto lds_store = [&](auto stage_c) __attribute__((always_inline)) {
@@ -398,17 +387,17 @@ __global__ __launch_bounds__(kThreads, P == kDV ? 3 : 2) void attn_bwd_kv_kernel
     if (tid < BQ) {
       *reinterpret_cast<float*>(lds + base + S_::L_OFF + tid * 4) =
           lse_log2(__uint_as_float(lraw), lvalid);
-      if constexpr (S_::kDelta) *reinterpret_cast<uint32_t*>(lds + base + S_::D_OFF + tid * 4) = draw;
+      *reinterpret_cast<uint32_t*>(lds + base + S_::D_OFF + tid * 4) = draw;
     }
   };
   const uint32_t r_rd = (uint32_t)(col * KS + 8 * half) * 2;
   const uint32_t t_rd = tr_lane_off<G::TS>(lane);
 
-  f32x16 dkacc[kWantDK ? D / 32 : 1], dvacc[kWantDV ? D / 32 : 1];
+  f32x16 dkacc[D / 32], dvacc[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) {
-    if constexpr (kWantDK) dkacc[db] = f32x16{};
-    if constexpr (kWantDV) dvacc[db] = f32x16{};
+    dkacc[db] = f32x16{};
+    dvacc[db] = f32x16{};
   }
 
   auto step = [&](int t, auto stage_c) __attribute__((always_inline)) {
@@ -420,40 +409,37 @@ __global__ __launch_bounds__(kThreads, P == kDV ? 3 : 2) void attn_bwd_kv_kernel
     // Some query of the tile sees a key of this wave.
     if (!CAUSAL || q0 + BQ - 1 + off >= kw) {
       // S = Q K^T (and dP = dO V^T for dK), 32 queries per accumulator.
-      f32x16 sacc[NQB], pacc[kWantDK ? NQB : 1];
+      f32x16 sacc[NQB], pacc[NQB];
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb) {
         sacc[qb] = f32x16{};
-        if constexpr (kWantDK) pacc[qb] = f32x16{};
+        pacc[qb] = f32x16{};
 #pragma unroll
         for (int j = 0; j < D / 16; ++j) {
           const uint32_t at = base + r_rd + (32 * qb * KS + 16 * j) * 2;
           sacc[qb] = Elem<E>::mfma(*reinterpret_cast<const v8*>(lds + at), kf[j], sacc[qb]);
-          if constexpr (kWantDK)
-            pacc[qb] = Elem<E>::mfma(*reinterpret_cast<const v8*>(lds + at + S_::DO_OFF),
-                                     vf[j], pacc[qb]);
+          pacc[qb] = Elem<E>::mfma(*reinterpret_cast<const v8*>(lds + at + S_::DO_OFF),
+                                   vf[j], pacc[qb]);
         }
       }
       // Register i of block qb holds query q0 + 32qb + 8(i/4) + 4h + i%4: its
       // lse and D come four at a time from LDS.
       const bool masked = CAUSAL && q0 + off < kw + 31;
-      v8 pb[kWantDV ? NQB : 1][2], dsb[kWantDK ? NQB : 1][2];
+      v8 pb[NQB][2], dsb[NQB][2];
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int row = 32 * qb + 8 * r + 4 * half;
           const f32x4 l4 = *reinterpret_cast<const f32x4*>(lds + base + S_::L_OFF + row * 4);
-          f32x4 d4 = {};
-          if constexpr (kWantDK)
-            d4 = *reinterpret_cast<const f32x4*>(lds + base + S_::D_OFF + row * 4);
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(lds + base + S_::D_OFF + row * 4);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int i = 4 * r + e;
             float p = weight(sacc[qb][i], c, l4[e]);
             if (masked && kj > q0 + row + e + off) p = 0.f;
-            if constexpr (kWantDV) pb[qb][i >> 3][i & 7] = (E)p;
-            if constexpr (kWantDK) dsb[qb][i >> 3][i & 7] = (E)(p * (pacc[qb][i] - d4[e]));
+            pb[qb][i >> 3][i & 7] = (E)p;
+            dsb[qb][i >> 3][i & 7] = (E)(p * (pacc[qb][i] - d4[e]));
           }
         }
       // dV^T += dO^T P and dK^T += Q^T dS, 16 queries per MFMA.
@@ -463,14 +449,12 @@ __global__ __launch_bounds__(kThreads, P == kDV ? 3 : 2) void attn_bwd_kv_kernel
         for (int sg = 0; sg < 2; ++sg)
 #pragma unroll
           for (int db = 0; db < D / 32; ++db) {
-            if constexpr (kWantDV)
-              dvacc[db] = Elem<E>::mfma(
-                  tr_operand<v8, G::TS>(lds + base + S_::DOT_OFF, t_rd, 32 * qb + 16 * sg, 32 * db),
-                  pb[qb][sg], dvacc[db]);
-            if constexpr (kWantDK)
-              dkacc[db] = Elem<E>::mfma(
-                  tr_operand<v8, G::TS>(lds + base + S_::QT_OFF, t_rd, 32 * qb + 16 * sg, 32 * db),
-                  dsb[qb][sg], dkacc[db]);
+            dvacc[db] = Elem<E>::mfma(
+                tr_operand<v8, G::TS>(lds + base + S_::DOT_OFF, t_rd, 32 * qb + 16 * sg, 32 * db),
+                pb[qb][sg], dvacc[db]);
+            dkacc[db] = Elem<E>::mfma(
+                tr_operand<v8, G::TS>(lds + base + S_::QT_OFF, t_rd, 32 * qb + 16 * sg, 32 * db),
+                dsb[qb][sg], dkacc[db]);
           }
     }
 
@@ -501,16 +485,12 @@ __global__ __launch_bounds__(kThreads, P == kDV ? 3 : 2) void attn_bwd_kv_kernel
     for (int r = 0; r < 4; ++r) {
       const int at = (kj * D + 32 * db + 8 * r + 4 * half) * 2;
       v4 x4;
-      if constexpr (kWantDK) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x4[e] = (E)(dkacc[db][4 * r + e] * dk_scale);
-        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, x4), rdk, at, 0, 0);
-      }
-      if constexpr (kWantDV) {
+      for (int e = 0; e < 4; ++e) x4[e] = (E)(dkacc[db][4 * r + e] * dk_scale);
+      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, x4), rdk, at, 0, 0);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x4[e] = (E)dvacc[db][4 * r + e];
-        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, x4), rdv, at, 0, 0);
-      }
+      for (int e = 0; e < 4; ++e) x4[e] = (E)dvacc[db][4 * r + e];
+      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, x4), rdv, at, 0, 0);
     }
 }
 
@@ -546,7 +526,7 @@ hipError_t launch_bwd(const BwdArgs& a) {
   float* delta = a.delta;
   int BH = a.BH, Nq = a.Nq, Nk = a.Nk, nq = a.nq, nk = a.nk;
   float c = a.c, scale = a.scale;
-  // dQ (and D) first: the dK pass reads D.
+  // dQ (and D) first: the key-side kernel reads D.
   if (nq > 0) {
     void* args[] = {&q, &k, &v, &o, &lse, &d_o, &dq, &delta, &BH, &Nq, &Nk, &nq, &c, &scale};
     const hipError_t err =
@@ -559,16 +539,7 @@ hipError_t launch_bwd(const BwdArgs& a) {
     auto go = [&](const void* fn) {
       return hipLaunchKernel(fn, dim3(BH * nk), dim3(kThreads), args, 0, a.stream);
     };
-    // dK and dV in one pass where both accumulators fit two waves per SIMD;
-    // d=128: dV, then dK, each in its own pass.
-    if constexpr (kOnePass<D>) {
-      return go(reinterpret_cast<const void*>(&attn_bwd_kv_kernel<E, D, CAUSAL, kBoth>));
-    } else {
-      const hipError_t err =
-          go(reinterpret_cast<const void*>(&attn_bwd_kv_kernel<E, D, CAUSAL, kDV>));
-      if (err != hipSuccess) return err;
-      return go(reinterpret_cast<const void*>(&attn_bwd_kv_kernel<E, D, CAUSAL, kDK>));
-    }
+    return go(reinterpret_cast<const void*>(&attn_bwd_kv_kernel<E, D, CAUSAL>));
   }
   return hipSuccess;
 }
