@@ -12,12 +12,12 @@
 // one (batch, head); each wave owns 32 rows, and three (d=128) or four (d=64)
 // workgroups share a CU, so each SIMD holds waves of different workgroups
 // whose softmax (VALU) and matrix (MFMA) phases interleave. Keys and values
-// stream through LDS in tiles of 32 (d=128) or 64 (d=64) keys, HBM ->
-// registers -> LDS (K at d = 96 and 256 by buffer loads that write LDS
-// directly), double buffered one tile ahead with one barrier per tile.
-// Global loads are buffer loads: rows past N come back as zeros, with no
-// branches. Both contractions run on v_mfma_f32_32x32x16_bf16 in transposed
-// form:
+// stream through LDS in tiles of 32 (d=128) or 64 (d=64) keys, double
+// buffered one tile ahead with one barrier per tile: at d = 96 and 128 both,
+// and at d = 256 K, by buffer loads that write LDS directly (LDS DMA); the
+// rest HBM -> registers -> LDS. Global loads are buffer loads: rows past N
+// come back as zeros, with no branches. Both contractions run on
+// v_mfma_f32_32x32x16_bf16 in transposed form:
 //
 //   S^T (keys x queries) = K (keys x d) * Q^T (d x queries)
 //   O^T (d x queries)   += V^T (d x keys) * P^T (keys x queries)
