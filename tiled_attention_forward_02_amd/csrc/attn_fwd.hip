@@ -61,17 +61,20 @@ constexpr float kLazyMax = 8.0f;  // tolerated growth of the row max, log2 units
 constexpr float kLazySum = 4096.f;  // largest per-lane tile sum kept on a stale max
 // Softmax weights first, row maximum only when they grow too large, or row
 // maximum first. Weights first saves the max reduction: measured faster at
-// d = 96, 128 and 256; slower at d = 32 (-0.9% to -3.4%) and on the d = 64
-// workloads (B=4, H=16, N=1024 and causal B=8, H=16, N=2048), where the
-// extra live scores cost more than the reduction.
+// d = 64 to 256; at d = 32 slower (-0.9% to -3.4%), where the extra live
+// scores cost more than the reduction. At d = 64 it takes the kernel from 4
+// to 3 waves per SIMD and still wins (with the wave priority below, measured
+// interleaved: +2.0% on B=4 H=16 N=1024, +3.1% on B=16 H=16 N=4096, +3.8% on
+// the long causal shape, -0.7% on causal B=8 H=16 N=2048).
 template <int D>
-constexpr bool kSpeculativeWeights = D >= 96;
+constexpr bool kSpeculativeWeights = D >= 64;
 // Raise a wave's priority while it issues its two MFMA chains (and drop it
 // for the softmax and the staging), so that when several waves of a SIMD
 // have work the matrix pipe is fed first: +1.2-2.2% at d = 128 (measured
-// interleaved against the plain kernel), not kept at d <= 64 (0 to -3%).
+// interleaved against the plain kernel); at d = 64 with weights first part
+// of the gain above; at d = 32 not kept.
 template <int D>
-constexpr bool kMfmaPriority = D >= 96;
+constexpr bool kMfmaPriority = D >= 64;
 // Stage K and V by buffer loads that write LDS directly (no registers, no
 // LDS write instructions) instead of through registers. Timing copies that
 // drop the global loads but keep the LDS writes ran 16% faster at d = 128:
