@@ -1,7 +1,8 @@
 // common.h - device helpers shared by the attention forward and backward
 // kernels for gfx950 (CDNA4): element types and their MFMA, buffer resources,
-// lane-half exchange, the key order inside a 16-key slice, the V^T / Q^T LDS
-// swizzle and the workgroup -> tile mapping.
+// LDS DMA of row-major tiles, transposing LDS reads and their row pitch,
+// lane-half exchange, the key order inside a 16-key slice and the workgroup
+// -> tile mapping.
 //
 // MFMA 32x32x16 fragment layout used throughout (lane l, h = l / 32, c = l % 32):
 //   A (32 x 16):  lane holds row c, k-elements 8h .. 8h+7
@@ -61,17 +62,6 @@ constexpr int kThreads = 64 * kWaves;  // threads per workgroup
 // inverse.
 __device__ __forceinline__ int slice_pos(int o) {
   return (o & 3) | ((o & 4) << 1) | ((o & 8) >> 1);
-}
-
-// XOR swizzle of the 16-byte blocks of a transposed tile's row (BN/8 blocks),
-// a function of the row index mod 32 only (the same for every 32-row block a
-// lane reads). Chosen by measurement (SQ_LDS_BANK_CONFLICT on gfx950): with
-// 64-byte rows (BN = 32) any function of bits 0, 1, 3 alone left 4 conflict
-// cycles on every 8-cycle operand read; keying on bit 2 removes them all.
-template <int BN>
-__device__ __forceinline__ int vt_swz(int d) {
-  d &= 31;
-  return BN >= 64 ? ((d ^ (d >> 3)) & 7) : ((d >> 2) & 3);
 }
 
 // Workgroup id -> (batch*head, tile). Workgroups are dealt to the 8 XCDs
