@@ -82,11 +82,16 @@ constexpr bool kMfmaPriority = D >= 64;
 // interleaved against the register path: K and V by DMA +2.2% at d = 128,
 // +3.8% on the long causal workload, +7.5% at d = 96 (its kernel drops to
 // 127 VGPRs, four waves per SIMD); at d = 256 K alone (+3.1%; V too -2.9%);
-// at d = 32 and 64 neither (-1% to -4%).
+// at d = 64, with four waves per SIMD forced (kMinBlocks), +0.8% to +3.3%
+// on four shapes (without the fourth wave -1.4% to +0.8%); at d = 32 DMA
+// loses (-1%).
 template <int D>
-constexpr bool kKDma = D == 96 || D == 128 || D == 256;
+constexpr bool kKDma = D == 64 || D == 96 || D == 128 || D == 256;
 template <int D>
-constexpr bool kVDma = D == 96 || D == 128;
+constexpr bool kVDma = D == 64 || D == 96 || D == 128;
+// Workgroups per CU the register allocation must allow.
+template <int D>
+constexpr int kMinBlocks = D == 256 ? 1 : D == 64 ? 4 : D >= 96 ? 3 : 2;
 
 constexpr int kBlockM = 32 * kWaves;   // query rows per workgroup
 // Keys per tile for head dimension D. At d=128 a 32-key tile keeps a wave
@@ -130,7 +135,7 @@ struct Tile {
 };
 
 template <typename E, int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, D == 256 ? 1 : D >= 96 ? 3 : 2) void attn_fwd_kernel(
+__global__ __launch_bounds__(kThreads, kMinBlocks<D>) void attn_fwd_kernel(
     const E* __restrict__ Q, const E* __restrict__ K,
     const E* __restrict__ V, E* __restrict__ O,
     float* __restrict__ LSE, int BH, int Nq, int Nk, int nq, float c) {
