@@ -191,7 +191,6 @@ __global__ __launch_bounds__(kThreads, kMinBlocks<D>) void attn_fwd_kernel(
 #pragma unroll
   for (int s = 0; s < D / 16; ++s) qf[s] = __builtin_bit_cast(v8, qraw[s]);
 
-  // Keys this workgroup / this wave can see.
   // Keys this workgroup / this wave can see (none for rows before -off).
   const int kv_end = CAUSAL ? min(Nk, q0 + kBlockM + off) : Nk;
   const int nt = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
@@ -199,47 +198,19 @@ __global__ __launch_bounds__(kThreads, kMinBlocks<D>) void attn_fwd_kernel(
 
   char* const lds = reinterpret_cast<char*>(smem);
 
-  // Staging by DMA: straight from HBM into LDS (16 bytes a lane, no
-  // registers). A tile in LDS is BN rows of row_slots 16-byte slots (the
-  // row's data chunks, then its pad); one wave instruction writes 64
-  // consecutive slots at its LDS base, lane l the slot 64 u + l of
-  // instruction u (u = wave, wave + 4, ...; whether u is in the tile is a
-  // uniform branch). Lanes of pad slots, of chunks past the data (d = 96)
-  // and past the tile get an offset beyond any buffer, which the range check
-  // turns into zeros without a fetch, so no lane is masked: the last
-  // instruction of a K tile writes its padding. The tile's first key goes
-  // into the vector offset, so the range check still zero-fills rows past
-  // Nk.
-  constexpr uint32_t kNoFetch = 0x80000000u;  // + k0 * D * 2 < 2^31: no wrap
-  constexpr int KROW_SLOTS = KS / 8, VROW_SLOTS = T::VS / 8;
-  constexpr int KINSTR = (BN * KROW_SLOTS + 63) / 64;      // per tile
-  constexpr int VINSTR = (BN * VROW_SLOTS + 63) / 64;
-  constexpr int KI_W = (KINSTR + kWaves - 1) / kWaves;     // per wave
-  constexpr int VI_W = (VINSTR + kWaves - 1) / kWaves;
-  static_assert(KINSTR * 512 <= T::K_SPAN, "K DMA stays within the K span");
-  static_assert(!kVDma<D> || VINSTR * 512 == T::V_ELEMS, "V DMA covers the V tile exactly");
+  // Staging by DMA (DmaTile): K and V tiles straight from HBM into LDS, no
+  // registers; the K tile's LDS span is rounded up to 1024 bytes for it.
+  typedef DmaTile<D, BN, KS> KDma;
+  typedef DmaTile<D, BN, T::VS> VDma;
+  static_assert(KDma::SPAN == T::K_SPAN * 2, "K DMA span is the K tile's LDS span");
+  static_assert(!kVDma<D> || VDma::SPAN == T::V_ELEMS * 2, "V DMA covers the V tile exactly");
   lds_char* const lds3 = to_lds(smem);
-  auto dma_off = [&](int u, int row_slots) {
-    const int slot = 64 * u + lane, row = slot / row_slots, ch = slot % row_slots;
-    return row < BN && ch < CPR_DATA ? (uint32_t)(row * D + 8 * ch) * 2 : kNoFetch;
-  };
-  uint32_t kdma_off[KI_W], vdma_off[VI_W];
-#pragma unroll
-  for (int i = 0; i < KI_W; ++i) kdma_off[i] = dma_off(wave + kWaves * i, KROW_SLOTS);
-#pragma unroll
-  for (int i = 0; i < VI_W; ++i) vdma_off[i] = dma_off(wave + kWaves * i, VROW_SLOTS);
-  auto dma_tile = [&](rsrc_t r, uint32_t tile, const uint32_t* offs, int ninstr, int nw, int k0)
-      __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < nw; ++i) {
-      const int u = wave + kWaves * i;
-      if (u < ninstr) load16_lds(r, lds3 + tile + 1024 * u, offs[i] + (uint32_t)k0 * D * 2);
-    }
-  };
+  const KDma kdma(wave, lane);
+  const VDma vdma(wave, lane);
   auto dma = [&](auto stage_c, int k0) {
     constexpr uint32_t base = decltype(stage_c)::value * T::STAGE * 2;
-    if constexpr (kKDma<D>) dma_tile(rk, base, kdma_off, KINSTR, KI_W, k0);
-    if constexpr (kVDma<D>) dma_tile(rv, base + T::K_SPAN * 2, vdma_off, VINSTR, VI_W, k0);
+    if constexpr (kKDma<D>) kdma.issue(rk, lds3 + base, wave, k0);
+    if constexpr (kVDma<D>) vdma.issue(rv, lds3 + base + T::K_SPAN * 2, wave, k0);
   };
 
   // Staging through registers: thread owns rows kr .. kr+KPT-1 and 16-byte
