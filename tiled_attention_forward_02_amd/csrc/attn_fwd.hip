@@ -239,13 +239,9 @@ __global__ __launch_bounds__(kThreads, kMinBlocks<D>) void attn_fwd_kernel(
   const uint32_t k_wr = (uint32_t)(kr * KS + 8 * dc) * 2;
   const uint32_t v_wr = (uint32_t)(T::K_SPAN + kr * T::VS + 8 * dc) * 2;
   const uint32_t k_rd = (uint32_t)(col * KS + 8 * half) * 2;
-  // V^T fragment of a 16-key slice and 32 columns: two transposing reads, 8
-  // keys apart. Lane 16 g + s points at row 4 (g / 2) + s / 4, columns
-  // 16 (g % 2) + 4 (s % 4) .. +3 of the slice; it then holds column
-  // col of keys 4 half .. 4 half + 3 (and 8 further with the second read),
-  // the keys its P^T register slots carry (see slice_pos).
-  const uint32_t v_rd = (uint32_t)(T::K_SPAN + (4 * half + ((lane & 15) >> 2)) * T::VS +
-                                   16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
+  // V^T operands come from transposing reads of the row-major V tile, two
+  // per 16-key slice (tr_operand): the keys in the order of the P^T slots.
+  const uint32_t v_rd = (uint32_t)T::K_SPAN * 2 + tr_lane_off<T::VS>(lane);
 
   auto lds_store = [&](auto stage_c) {
     constexpr uint32_t base = decltype(stage_c)::value * T::STAGE * 2;
@@ -379,9 +375,7 @@ __global__ __launch_bounds__(kThreads, kMinBlocks<D>) void attn_fwd_kernel(
         for (int sg = 0; sg < 2; ++sg) {
 #pragma unroll
           for (int db = 0; db < D / 32; ++db) {
-            const char* p = lds + base + v_rd + ((32 * kb + 16 * sg) * T::VS + 32 * db) * 2;
-            const u32x2 lo = lds_read_tr16(p), hi = lds_read_tr16(p + 8 * T::VS * 2);
-            const v8 a = __builtin_bit_cast(v8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+            const v8 a = tr_operand<v8, T::VS>(lds + base, v_rd, 32 * kb + 16 * sg, 32 * db);
             oacc[db] = Elem<E>::mfma(a, pb[kb][sg], oacc[db]);
           }
         }

@@ -184,6 +184,29 @@ __device__ __forceinline__ float neg_inf_where(int masked, float x) {
   return r;
 }
 
+// Byte offset, within a row-major tile of pitch TS, of this lane's address
+// for lds_read_tr16 reads of the MFMA A operand of a 16-row slice: lane
+// 16 g + s points at row 4 (g / 2) + s / 4, columns 16 (g % 2) + 4 (s % 4)
+// .. +3, and then holds column lane % 32 of rows 4 h .. 4 h + 3 of the slice
+// (h = lane / 32); a second read 8 rows further gives rows 8 + 4 h ..
+// 8 + 4 h + 3. Those are the rows that the B operand's slots 0-7 carry
+// (slice_pos order).
+template <int TS>
+__device__ __forceinline__ uint32_t tr_lane_off(int lane) {
+  return (uint32_t)((4 * (lane >> 5) + ((lane & 15) >> 2)) * TS + 16 * ((lane >> 4) & 1) +
+                    4 * (lane & 3)) * 2;
+}
+
+// The 8-element A operand of rows `row0` .. row0 + 15 (a 16-row slice) and
+// columns `col0` .. col0 + 31 from a copy for transposing reads at `tile`.
+template <typename V8, int TS>
+__device__ __forceinline__ V8 tr_operand(const char* tile, uint32_t lane_off, int row0,
+                                         int col0) {
+  const char* p = tile + lane_off + (row0 * TS + col0) * 2;
+  const u32x2 lo = lds_read_tr16(p), hi = lds_read_tr16(p + 8 * TS * 2);
+  return __builtin_bit_cast(V8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+}
+
 // Value of x in the lane 32 positions away, combined with op (same result in
 // both lanes of the pair, bit for bit).
 __device__ __forceinline__ float swap_halves_max(float x) {
