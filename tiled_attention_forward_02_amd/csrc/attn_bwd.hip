@@ -61,22 +61,73 @@ constexpr int kTileRows = D <= 64 ? 64 : 32;
 template <int D>
 constexpr int kLayoutD = D == 96 ? 128 : D;
 
-// A tile of BR rows of a [*, D] tensor in LDS, in up to two row-major
-// copies: pitch DL + 8 for 16-byte row reads (the 16-byte pad puts the 16
-// rows one read pass touches on distinct banks), and tr_pitch for
-// transposing reads. Each copy is loaded by LDS DMA (DmaTile) straight from
-// the tensor and takes a multiple of 1024 bytes of LDS (its DMA span).
-template <int D, int BR_>
-struct Rows {
+// A tile of BR rows of a [*, D] tensor in LDS: one row-major copy that
+// serves both 16-byte row reads (an MFMA A operand of rows) and transposing
+// reads (lds_read_tr16: an A operand of columns). Row pitch P elements is an
+// odd multiple of 64 bytes, and the 16-byte chunk c of row r sits at chunk
+// c ^ ((r >> 2) & 3). With the LDS's 64 banks of 4 bytes:
+//  * a transposing-read pass (32 lanes) covers 4 consecutive rows x one
+//    64-byte group of 4 chunks; the swizzle permutes chunks only within a
+//    group, and the rows' groups start 64 bytes apart mod 256: no conflict;
+//  * a row-read pass (16 lanes, 16 bytes each) covers 16 rows at one
+//    chunk; the pitch alone would put them in 4 bank groups, the swizzle
+//    spreads them over all 16.
+// The tile is loaded by LDS DMA, the swizzle applied through each lane's
+// source offset; it takes SPAN bytes of LDS (a multiple of 1024). Each lane
+// keeps its DMA offsets, two row-read bases (the chunk pair's low bits XOR
+// the swizzle take two values) and two transposing-read offsets (rows +0
+// and +8 of a slice).
+template <int D, int BR>
+struct SwzTile {
   static constexpr int DL = kLayoutD<D>;
-  static constexpr int BR = BR_;
-  static constexpr int KS = DL + 8;
-  static constexpr int TS = tr_pitch<DL>();
-  typedef DmaTile<D, BR, KS> RowDma;
-  typedef DmaTile<D, BR, TS> TrDma;
-  static constexpr int ROW_SPAN = RowDma::SPAN;  // bytes, copy for row reads
-  static constexpr int TR_SPAN = TrDma::SPAN;    // bytes, copy for transposing reads
-  static_assert(ROW_SPAN >= BR * KS * 2 && TR_SPAN >= BR * TS * 2, "DMA spans hold the tiles");
+  static constexpr int P = DL % 64 == 32 ? DL : DL + 32;  // row pitch, elements
+  static constexpr int SLOTS = P / 8, CPR = DL / 8;
+  static constexpr int NINSTR = (BR * SLOTS + 63) / 64;
+  static constexpr int NW = (NINSTR + kWaves - 1) / kWaves;  // per wave, at most
+  static constexpr int SPAN = NINSTR * 1024;
+  static constexpr uint32_t kNoFetch = 0x80000000u;  // + row0 * D * 2 < 2^31
+  static_assert((P * 2) % 128 == 64, "pitch: an odd multiple of 64 bytes");
+  uint32_t off[NW];
+  uint32_t rrd[2], trd[2];
+  static __device__ __forceinline__ int swz(int row) { return (row >> 2) & 3; }
+  __device__ __forceinline__ SwzTile(int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+      const int slot = 64 * (wave + kWaves * i) + lane;
+      const int row = slot / SLOTS, pc = slot % SLOTS;
+      const int c = pc ^ swz(row);  // logical chunk held by physical chunk pc
+      off[i] = row < BR && pc < CPR && c < D / 8 ? (uint32_t)(row * D + 8 * c) * 2 : kNoFetch;
+    }
+    const int col = lane & 31, h = lane >> 5, g = lane >> 4, s = lane & 15;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      rrd[e] = (uint32_t)(col * P + 8 * ((2 * e + h) ^ swz(col))) * 2;
+      trd[e] = (uint32_t)((4 * (g >> 1) + (s >> 2) + 8 * e) * P +
+                          8 * ((2 * (g & 1) + ((s & 3) >> 1)) ^ (((g >> 1) + 2 * e) & 3)) +
+                          4 * (s & 1)) * 2;
+    }
+  }
+  __device__ __forceinline__ void issue(rsrc_t r, lds_char* tile, int wave, int row0) const {
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+      const int u = wave + kWaves * i;
+      if (u < NINSTR) load16_lds(r, tile + 1024 * u, off[i] + (uint32_t)row0 * D * 2);
+    }
+  }
+  // A operand of rows 32 blk + lane % 32, k-elements 16 j + 8 h .. +7.
+  template <typename V8>
+  __device__ __forceinline__ V8 rows(const char* tile, int blk, int j) const {
+    return *reinterpret_cast<const V8*>(tile + rrd[j & 1] + (32 * blk * P + 32 * (j >> 1)) * 2);
+  }
+  // A operand of columns col0 .. col0 + 31 over rows row0 .. row0 + 15 (a
+  // 16-row slice, row0 a multiple of 16), rows in slice_pos order: the lane
+  // layout of tr_lane_off, with each lane's chunk moved by the swizzle.
+  template <typename V8>
+  __device__ __forceinline__ V8 cols(const char* tile, int row0, int col0) const {
+    const char* q = tile + (row0 * P + col0) * 2;
+    const u32x2 lo = lds_read_tr16(q + trd[0]), hi = lds_read_tr16(q + trd[1]);
+    return __builtin_bit_cast(V8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+  }
 };
 
 // 2^(s*c - l2), the weight of a score s given the row's lse in log2 units.
@@ -99,11 +150,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(
     E* __restrict__ dQ, float* __restrict__ Delta, int BH, int Nq, int Nk, int nq, float c,
     float dq_scale) {
   constexpr int BN = kTileRows<D>;
-  using G = Rows<D, BN>;
-  constexpr int KS = G::KS, NKB = BN / 32;
-  // Stage: K rows | V rows | K for transposing reads.
-  constexpr int V_OFF = G::ROW_SPAN, KT_OFF = 2 * G::ROW_SPAN;
-  constexpr int STAGE = 2 * G::ROW_SPAN + G::TR_SPAN;
+  using G = SwzTile<D, BN>;
+  constexpr int NKB = BN / 32;
+  // Stage: K | V (K is read both as rows and as columns).
+  constexpr int V_OFF = G::SPAN;
+  constexpr int STAGE = 2 * G::SPAN;
   typedef typename Elem<E>::v8 v8;
   typedef typename Elem<E>::v4 v4;
   __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
@@ -156,20 +207,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(
   const int nt = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
   const int wave_kv_end = CAUSAL ? min(Nk, qw + 32 + off) : Nk;
 
-  // The key tile from k0 into a stage, by DMA (K twice: rows and the copy
-  // for transposing reads).
-  const typename G::RowDma row_dma(wave, lane);
-  const typename G::TrDma tr_dma(wave, lane);
+  // The key tile from k0 into a stage, by DMA.
+  const G tile(wave, lane);
   char* const lds = smem;
   lds_char* const lds3 = to_lds(smem);
   auto stage_tile = [&](auto stage_c, int k0) __attribute__((always_inline)) {
     constexpr uint32_t base = decltype(stage_c)::value * STAGE;
-    row_dma.issue(rk, lds3 + base, wave, k0);
-    row_dma.issue(rv, lds3 + base + V_OFF, wave, k0);
-    tr_dma.issue(rk, lds3 + base + KT_OFF, wave, k0);
+    tile.issue(rk, lds3 + base, wave, k0);
+    tile.issue(rv, lds3 + base + V_OFF, wave, k0);
   };
-  const uint32_t r_rd = (uint32_t)(col * KS + 8 * half) * 2;
-  const uint32_t t_rd = tr_lane_off<G::TS>(lane);
 
   f32x16 acc[D / 32];
 #pragma unroll
@@ -190,9 +236,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(
         pacc[kb] = f32x16{};
 #pragma unroll
         for (int j = 0; j < D / 16; ++j) {
-          const uint32_t at = base + r_rd + (32 * kb * KS + 16 * j) * 2;
-          sacc[kb] = Elem<E>::mfma(*reinterpret_cast<const v8*>(lds + at), qf[j], sacc[kb]);
-          pacc[kb] = Elem<E>::mfma(*reinterpret_cast<const v8*>(lds + at + V_OFF), df[j],
+          sacc[kb] = Elem<E>::mfma(tile.template rows<v8>(lds + base, kb, j), qf[j], sacc[kb]);
+          pacc[kb] = Elem<E>::mfma(tile.template rows<v8>(lds + base + V_OFF, kb, j), df[j],
                                    pacc[kb]);
         }
       }
@@ -223,8 +268,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(
         for (int sg = 0; sg < 2; ++sg)
 #pragma unroll
           for (int db = 0; db < D / 32; ++db) {
-            const v8 a = tr_operand<v8, G::TS>(lds + base + KT_OFF, t_rd, 32 * kb + 16 * sg,
-                                               32 * db);
+            const v8 a = tile.template cols<v8>(lds + base, 32 * kb + 16 * sg, 32 * db);
             acc[db] = Elem<E>::mfma(a, dsb[kb][sg], acc[db]);
           }
     }
@@ -267,16 +311,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(
 // d = 128, with two values spilled outside the loop).
 
 // LDS stage of the key-side kernel:
-//   Q rows (S = Q K^T) | dO rows (dP) | Q for transposing reads (dK) |
-//   dO for transposing reads (dV) | lse | D (dS)
+//   Q (rows: S = Q K^T; columns: dK) | dO (rows: dP; columns: dV) | lse | D
 template <int D>
 struct KeyStage {
-  using G = Rows<D, kTileRows<D>>;
-  static constexpr int BQ = G::BR;
-  static constexpr int DO_OFF = G::ROW_SPAN;
-  static constexpr int QT_OFF = DO_OFF + G::ROW_SPAN;
-  static constexpr int DOT_OFF = QT_OFF + G::TR_SPAN;
-  static constexpr int L_OFF = DOT_OFF + G::TR_SPAN;
+  static constexpr int BQ = kTileRows<D>;
+  using G = SwzTile<D, BQ>;
+  static constexpr int DO_OFF = G::SPAN;
+  static constexpr int L_OFF = 2 * G::SPAN;
   static constexpr int D_OFF = L_OFF + BQ * 4;
   static constexpr int BYTES = D_OFF + BQ * 4;
   static_assert(BYTES % 16 == 0 && L_OFF % 16 == 0, "16-byte aligned LDS tiles");
@@ -291,7 +332,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_kv_kernel(
   using S_ = KeyStage<D>;
   using G = typename S_::G;
   constexpr int BQ = S_::BQ;
-  constexpr int KS = G::KS, NQB = BQ / 32;
+  constexpr int NQB = BQ / 32;
   constexpr int STAGE = S_::BYTES;
   typedef typename Elem<E>::v8 v8;
   typedef typename Elem<E>::v4 v4;
@@ -341,18 +382,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_kv_kernel(
   // tid < BQ) through registers, kept raw until written to LDS at the end of
   // the step: using them at once would wait for every load in flight, the
   // tile's own included.
-  const typename G::RowDma row_dma(wave, lane);
-  const typename G::TrDma tr_dma(wave, lane);
+  const G tile(wave, lane);
   char* const lds = smem;
   lds_char* const lds3 = to_lds(smem);
   uint32_t lraw = 0, draw = 0;
   bool lvalid = false;
   auto gload = [&](auto stage_c, int q0) __attribute__((always_inline)) {
     constexpr uint32_t base = decltype(stage_c)::value * STAGE;
-    row_dma.issue(rq, lds3 + base, wave, q0);
-    row_dma.issue(rdo, lds3 + base + S_::DO_OFF, wave, q0);
-    tr_dma.issue(rq, lds3 + base + S_::QT_OFF, wave, q0);
-    tr_dma.issue(rdo, lds3 + base + S_::DOT_OFF, wave, q0);
+    tile.issue(rq, lds3 + base, wave, q0);
+    tile.issue(rdo, lds3 + base + S_::DO_OFF, wave, q0);
     if (tid < BQ) {
       const int qrow = q0 + tid;
       lvalid = qrow < Nq;
@@ -368,9 +406,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_kv_kernel(
       *reinterpret_cast<uint32_t*>(lds + base + S_::D_OFF + tid * 4) = draw;
     }
   };
-  const uint32_t r_rd = (uint32_t)(col * KS + 8 * half) * 2;
-  const uint32_t t_rd = tr_lane_off<G::TS>(lane);
-
   f32x16 dkacc[D / 32], dvacc[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) {
@@ -394,9 +429,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_kv_kernel(
         pacc[qb] = f32x16{};
 #pragma unroll
         for (int j = 0; j < D / 16; ++j) {
-          const uint32_t at = base + r_rd + (32 * qb * KS + 16 * j) * 2;
-          sacc[qb] = Elem<E>::mfma(*reinterpret_cast<const v8*>(lds + at), kf[j], sacc[qb]);
-          pacc[qb] = Elem<E>::mfma(*reinterpret_cast<const v8*>(lds + at + S_::DO_OFF),
+          sacc[qb] = Elem<E>::mfma(tile.template rows<v8>(lds + base, qb, j), kf[j], sacc[qb]);
+          pacc[qb] = Elem<E>::mfma(tile.template rows<v8>(lds + base + S_::DO_OFF, qb, j),
                                    vf[j], pacc[qb]);
         }
       }
@@ -428,11 +462,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_kv_kernel(
 #pragma unroll
           for (int db = 0; db < D / 32; ++db) {
             dvacc[db] = Elem<E>::mfma(
-                tr_operand<v8, G::TS>(lds + base + S_::DOT_OFF, t_rd, 32 * qb + 16 * sg, 32 * db),
+                tile.template cols<v8>(lds + base + S_::DO_OFF, 32 * qb + 16 * sg, 32 * db),
                 pb[qb][sg], dvacc[db]);
-            dkacc[db] = Elem<E>::mfma(
-                tr_operand<v8, G::TS>(lds + base + S_::QT_OFF, t_rd, 32 * qb + 16 * sg, 32 * db),
-                dsb[qb][sg], dkacc[db]);
+            dkacc[db] = Elem<E>::mfma(tile.template cols<v8>(lds + base, 32 * qb + 16 * sg, 32 * db),
+                                      dsb[qb][sg], dkacc[db]);
           }
     }
 
