@@ -117,23 +117,22 @@ __device__ __forceinline__ void load16_lds(rsrc_t r, lds_char* lds_base, uint32_
       r, (__attribute__((address_space(3))) void*)lds_base, 16, (int)byte_off, 0, 0, 0);
 }
 
-// LDS DMA of one row-major tile: rows row0 .. row0 + BR - 1 of a [*, D]
-// tensor (16-bit elements) into BR rows of PITCH elements, PITCH / 8
-// 16-byte slots a row of which D / 8 hold data. Instruction u of the tile
-// (u = wave, wave + kWaves, ...; whether u exists is a uniform branch)
-// writes slots 64 u .. 64 u + 63, lane l slot 64 u + l; lanes of pad slots,
-// of chunks past the data and past the tile get an offset beyond any buffer
-// (zeros, no fetch). The instructions write SPAN bytes from the tile's
-// start, a multiple of 1024 that the caller's layout reserves. Rows past the
-// buffer's end are zero-filled by the range check (the first row goes into
-// the vector offset).
+// LDS DMA of one row-major tile: the first BR rows of a [*, D] tensor (16-bit
+// elements) that a buffer resource starts at, into BR rows of PITCH
+// elements, PITCH / 8 16-byte slots a row of which D / 8 hold data.
+// Instruction u of the tile (u = wave, wave + kWaves, ...; whether u exists
+// is a uniform branch) writes slots 64 u .. 64 u + 63, lane l slot
+// 64 u + l; lanes of pad slots, of chunks past the data and past the tile
+// get an offset beyond any buffer (zeros, no fetch). The instructions write
+// SPAN bytes from the tile's start, a multiple of 1024 that the caller's
+// layout reserves.
 template <int D, int BR, int PITCH>
 struct DmaTile {
   static constexpr int SLOTS = PITCH / 8;
   static constexpr int NINSTR = (BR * SLOTS + 63) / 64;
   static constexpr int NW = (NINSTR + kWaves - 1) / kWaves;  // per wave, at most
   static constexpr int SPAN = NINSTR * 1024;
-  static constexpr uint32_t kNoFetch = 0x80000000u;  // + row0 * D * 2 < 2^31
+  static constexpr uint32_t kNoFetch = 0x80000000u;  // > any head's bytes
   uint32_t off[NW];
   __device__ __forceinline__ DmaTile(int wave, int lane) {
 #pragma unroll
@@ -143,11 +142,14 @@ struct DmaTile {
       off[i] = row < BR && ch < D / 8 ? (uint32_t)(row * D + 8 * ch) * 2 : kNoFetch;
     }
   }
-  __device__ __forceinline__ void issue(rsrc_t r, lds_char* tile, int wave, int row0) const {
+  // r_tile's base is the tile's first row (its records counted from there):
+  // the per-lane offsets are fixed, so placing a tile is scalar work. Rows
+  // past the buffer's end are zero-filled by the range check.
+  __device__ __forceinline__ void issue(rsrc_t r_tile, lds_char* tile, int wave) const {
 #pragma unroll
     for (int i = 0; i < NW; ++i) {
       const int u = wave + kWaves * i;
-      if (u < NINSTR) load16_lds(r, tile + 1024 * u, off[i] + (uint32_t)row0 * D * 2);
+      if (u < NINSTR) load16_lds(r_tile, tile + 1024 * u, off[i]);
     }
   }
 };
