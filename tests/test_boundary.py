@@ -185,6 +185,17 @@ def test_cross_negative_lengths(lib, Nq, Nk):
     assert cross(lib, Nq=Nq, Nk=Nk) == ERR_SHAPE
 
 
+@pytest.mark.parametrize("d", [32, 64, 96, 128, 256])
+def test_longest_accepted_key_axis(lib, d):
+    # One head's keys plus a 128-row tile of slack must stay below 2^31 bytes:
+    # the longest such Nk passes the size checks (and then fails on the null
+    # q), one more is rejected as a shape error.
+    longest = (2**31 - 1 - 128 * d * 2) // (d * 2)
+    assert cross(lib, q=None, Nk=longest, d=d) == ERR_NULL
+    assert cross(lib, q=None, Nk=longest + 1, d=d) == ERR_SHAPE
+    assert cross(lib, q=None, Nq=longest + 1, d=d) == ERR_SHAPE
+
+
 def test_cross_null_and_empty(lib):
     assert cross(lib, q=None) == ERR_NULL
     assert cross(lib, k=None) == ERR_NULL

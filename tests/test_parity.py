@@ -174,6 +174,55 @@ def test_other_scales(scale, causal):
     check(o, lse, o_ref, lse_ref, f"scale={scale}")
 
 
+def max_key_length(d):
+    """Largest Nk the library accepts at head dim d: one head's key tensor plus
+    one 128-row tile of slack must stay below 2^31 bytes (its buffer offsets
+    are 32-bit), as include/mi_attn.h states for ATTN_ERR_SHAPE."""
+    return (2**31 - 1 - 128 * d * 2) // (d * 2)
+
+
+@pytest.mark.parametrize("d", [32, 64, 96, 128, 256])
+def test_longest_key_axis(d):
+    """The longest key axis one head may have (K and V 2 GiB each), checked by
+    closed forms, since the oracle cannot hold these tensors: needles at keys
+    spread over the whole axis, its last row included, and Q = 0.
+
+    Query i (i < Nq <= d) is 32 e_i and its needle key is 32 e_i; every other
+    key is 0, so query i scores s = 1024 * scale on its needle and 0 on every
+    other key. Then o_i = v_needle (the other weights are below 2^-130) and
+    lse_i = s + ln(1 + (Nk - 1) e^-s). With Q = 0 every weight is 1:
+    o_i = mean of V, lse_i = ln Nk."""
+    Nk = max_key_length(d)
+    Nq = min(64, d)
+    announce(f"longest key axis: d={d} Nq={Nq} Nk={Nk}")
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(41 + d)
+    v = torch.randn((1, 1, Nk, d), generator=g, device=dev, dtype=torch.float32)
+    v = (v + 1.0).to(torch.bfloat16)
+    k = torch.zeros((1, 1, Nk, d), device=dev, dtype=torch.bfloat16)
+    q = torch.zeros((1, 1, Nq, d), device=dev, dtype=torch.bfloat16)
+    half = Nq // 2
+    # the second half of the needles sits in the last tile, up to row Nk - 1
+    pos = [j * (Nk // half) + 7 * j for j in range(half)] + [Nk - 1 - j for j in range(Nq - half)]
+    for i, pj in enumerate(pos):
+        q[0, 0, i, i] = 32.0
+        k[0, 0, pj, i] = 32.0
+    scale = float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32))
+    o, lse = mi.attn_fwd_cross(q, k, v, scale=scale, causal=False)
+    torch.cuda.synchronize()
+    s = 1024.0 * scale
+    lse_ref = np.full(Nq, s + math.log1p((Nk - 1) * math.exp(-s)))
+    o_ref = v[0, 0, pos].double().cpu().numpy()
+    check(o[0, 0].float().cpu().numpy(), lse[0, 0].cpu().numpy(), o_ref, lse_ref,
+          f"needles, d={d}")
+    o0, lse0 = mi.attn_fwd_cross(torch.zeros_like(q), k, v, scale=scale, causal=False)
+    torch.cuda.synchronize()
+    mean = v[0, 0].mean(dim=0, dtype=torch.float64).cpu().numpy()
+    check(o0[0, 0].float().cpu().numpy(), lse0[0, 0].cpu().numpy(),
+          np.broadcast_to(mean, (Nq, d)), np.full(Nq, math.log(Nk)), f"Q = 0, d={d}")
+    del v, k
+
+
 def test_large_shift_of_keys():
     """A big common shift of all keys leaves O unchanged (needs the running
     maximum; scores reach about 2e2)."""
