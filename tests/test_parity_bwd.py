@@ -151,6 +151,52 @@ def test_bwd_other_scales(scale, causal):
 
 # --------------------------------------------------------------- edge cases --
 
+@pytest.mark.parametrize("d", [32, 64, 96, 128])
+def test_bwd_longest_key_axis(d):
+    """Gradients on the longest key axis one head may have (K, V, dK, dV
+    2 GiB each), checked by closed forms, since the oracle cannot hold these
+    tensors. Query i (i < Nq <= d) is 32 e_i and its needle key 32 e_i, every
+    other key 0: its weights are 1 on the needle and below 2^-130 elsewhere,
+    so o_i = v_needle, and with D_i = dO_i . o_i every dS vanishes. Then
+    dq = 0, dk = 0, and dv is dO_i on needle i's row and 0 on every other
+    row. The outputs start as NaN, so a row left unwritten fails."""
+    longest = (2**31 - 1 - 128 * d * 2) // (d * 2)
+    Nq = min(64, d)
+    announce(f"bwd longest key axis: d={d} Nq={Nq} Nk={longest}")
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(61 + d)
+    v = torch.randn((1, 1, longest, d), generator=g, device=dev,
+                    dtype=torch.float32).to(torch.bfloat16)
+    do = torch.randn((1, 1, Nq, d), generator=g, device=dev,
+                     dtype=torch.float32).to(torch.bfloat16)
+    k = torch.zeros((1, 1, longest, d), device=dev, dtype=torch.bfloat16)
+    q = torch.zeros((1, 1, Nq, d), device=dev, dtype=torch.bfloat16)
+    half = Nq // 2
+    pos = [j * (longest // half) + 7 * j for j in range(half)] + \
+          [longest - 1 - j for j in range(Nq - half)]
+    for i, pj in enumerate(pos):
+        q[0, 0, i, i] = 32.0
+        k[0, 0, pj, i] = 32.0
+    scale = float(torch.tensor(d ** -0.5, dtype=torch.float32))
+    o, lse = mi.attn_fwd_ex(q, k, v, scale=scale, causal=False)
+    nan = float("nan")
+    dq = torch.full_like(q, nan)
+    dk = torch.full_like(k, nan)
+    dv = torch.full_like(v, nan)
+    mi.attn_bwd(q, k, v, o, lse, do, scale=scale, causal=False, dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    dv_ref = torch.zeros_like(dv)
+    dv_ref[0, 0, pos] = do[0, 0]
+    errs = {"dq": float(dq.float().abs().max()),
+            "dk": float(dk.float().abs().max()),
+            "dv": float((dv.float() - dv_ref.float()).abs().max())}
+    print(f"  max errors {errs}", flush=True)
+    del k, dk, dv_ref
+    assert all(np.isfinite(x) for x in errs.values()), errs
+    assert errs["dq"] <= 1e-3 and errs["dk"] <= 1e-3, errs
+    assert errs["dv"] <= MAX_TOL * float(do.float().abs().max()), errs
+
+
 def test_bwd_one_side_empty():
     announce("bwd Nq=0 and Nk=0")
     dev = torch.device("cuda:0")
