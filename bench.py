@@ -67,11 +67,24 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def _code_text(name, raw):
+    """Source text with comments and blank lines dropped (C++ `//` comments in
+    the HIP sources, `#` comment lines in build.py), so that editing a comment
+    does not mark the profiles taken on that code as stale."""
+    text = raw.decode()
+    if name.endswith(".py"):
+        lines = [l for l in text.splitlines() if not l.lstrip().startswith("#")]
+    else:
+        lines = [re.sub(r"//.*$", "", l) for l in text.splitlines()]
+    return "\n".join(l.rstrip() for l in lines if l.strip()).encode()
+
+
 def kernel_sha(which="fwd"):
+    """Hash of the code each timed pass is built from (comments excluded)."""
     h = hashlib.sha256()
     for name in KERNEL_SRCS[which]:
         with open(os.path.join(PKG, name), "rb") as f:
-            h.update(f.read())
+            h.update(_code_text(name, f.read()))
     return h.hexdigest()[:16]
 
 

@@ -13,10 +13,11 @@
 // workgroups share a CU, so each SIMD holds waves of different workgroups
 // whose softmax (VALU) and matrix (MFMA) phases interleave. Keys and values
 // stream through LDS in tiles of 32 (d=128) or 64 (d=64) keys, double
-// buffered one tile ahead with one barrier per tile: at d = 96 and 128 both,
-// and at d = 256 K, by buffer loads that write LDS directly (LDS DMA); the
-// rest HBM -> registers -> LDS. Global loads are buffer loads: rows past N
-// come back as zeros, with no branches. Both contractions run on
+// buffered one tile ahead with one barrier per tile: at d = 64, 96 and 128
+// both, and at d = 256 K, by buffer loads that write LDS directly (LDS DMA),
+// each tile through a buffer resource based at its first row; the rest
+// HBM -> registers -> LDS. Global loads are buffer loads: rows past N come
+// back as zeros, with no branches. Both contractions run on
 // v_mfma_f32_32x32x16_bf16 in transposed form:
 //
 //   S^T (keys x queries) = K (keys x d) * Q^T (d x queries)
@@ -30,13 +31,16 @@
 // (ds_read_b64_tr_b16) hand each lane the V^T column it needs, 4 keys at a
 // time, in that permuted order.
 //
-// The running maximum is raised lazily: only when a tile's row maximum
-// exceeds it by more than 2^8 (log2 units) are O and the row sum rescaled;
-// otherwise the stale maximum is kept, the weights of that tile are at most
-// 2^8, and O / l and m + log2(l) stay exact in real arithmetic because O and
-// l always share one reference maximum. Masking (causal diagonal tiles and
-// the tile holding key N-1) is the only per-element select, and only those
-// tiles run it.
+// The running maximum is raised lazily. At d >= 64 the weights of a tile are
+// computed against the current reference maximum straight away, and the
+// reference moves (the tile's row maximum taken, O and the row sum rescaled,
+// the weights redone) only on the first tile or when a lane's share of the
+// tile's weights exceeds 2^12. At d = 32 the tile's row maximum comes first,
+// and the reference moves only when it exceeds the reference by more than
+// 2^8 (log2 units). Either way O / l and m + log2(l) stay exact in real
+// arithmetic, because O and l always share one reference maximum. Masking
+// (causal diagonal tiles and the tile holding key N-1) is the only
+// per-element select, and only those tiles run it.
 //
 // The MFMA fragment layout these comments refer to is described in common.h.
 
