@@ -58,7 +58,10 @@ typedef enum {
  *   d        head dimension: 32, 64, 96, 128 or 256.
  *   scale    softmax scale, applied to Q K^T before masking; used exactly as
  *            the given float32 value. Any finite value (0 and negative
- *            included) is accepted.
+ *            included) is accepted. The scaled scores are formed in float32
+ *            (times log2 e): where |scale * q_i . k_j| * log2 e exceeds the
+ *            float32 range the outputs are unspecified, and lse, a float32,
+ *            carries a rounding error relative to its own magnitude.
  *   causal   0: every key visible. Non-zero: key j visible to query i iff j <= i.
  *   stream   hipStream_t to launch on; NULL means the null stream.
  *
