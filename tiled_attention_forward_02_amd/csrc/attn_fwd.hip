@@ -9,9 +9,11 @@
 // signature on that same page (Out, Lse, softmax_scale, IS_CAUSAL).
 //
 // Design for MI355X (gfx950). One workgroup of 4 waves owns 128 query rows of
-// one (batch, head); each wave owns 32 rows, and three (d=128) or four (d=64)
-// workgroups share a CU, so each SIMD holds waves of different workgroups
-// whose softmax (VALU) and matrix (MFMA) phases interleave. Keys and values
+// one (batch, head), each wave 32 of them, or at d = 128 256 rows, each wave
+// two blocks of 32 that share every K and V fragment it reads from LDS. Two
+// (d=128), three (d=96) or four (d=64) workgroups share a CU, so each SIMD
+// holds waves of different workgroups whose softmax (VALU) and matrix (MFMA)
+// phases interleave. Keys and values
 // stream through LDS in tiles of 32 (d=128) or 64 (d=64) keys, double
 // buffered one tile ahead with one barrier per tile: at d = 64, 96 and 128
 // both, and at d = 256 K, by buffer loads that write LDS directly (LDS DMA),
@@ -100,13 +102,27 @@ constexpr bool kVDma = D == 64 || D == 96 || D == 128;
 // +2.3% and +1.8% on two non-causal d = 64 shapes, +2.8% at d = 96, +1.8% at
 // d = 256, and with the bit-select mask below +1.4% on causal d = 64.
 // Workgroups per CU the register allocation must allow.
+// 32-query blocks per wave. At d = 128 a wave owns two blocks (64 queries):
+// every K and V^T fragment it reads from LDS then serves both, which halves
+// the LDS read traffic per FLOP, and the kernel fits in 256 VGPRs, two waves
+// per SIMD. Under the power cap that beat three one-block waves per SIMD by
+// 6.1% on B=16 H=16 N=4096 (interleaved A/B, bit-identical outputs); on the
+// long causal shape the two were level. At d = 96 (-1.1%, -6%) and d = 64
+// (-12% on the two small workloads) the fourth one-block wave per SIMD is
+// worth more, so they keep one block.
 template <int D>
-constexpr int kMinBlocks = D == 256 ? 1 : D == 64 ? 4 : D >= 96 ? 3 : 2;
+constexpr int kQB = D == 128 ? 2 : 1;
+template <int D>
+constexpr int kMinBlocks = kQB<D> == 2 ? 2 : D == 256 ? 1 : D == 64 ? 4 : D >= 96 ? 3 : 2;
 
-constexpr int kBlockM = 32 * kWaves;   // query rows per workgroup
-// Keys per tile for head dimension D. At d=128 a 32-key tile keeps a wave
-// under 168 VGPRs and a workgroup at 33 KiB of LDS, so three workgroups
-// (three waves per SIMD) share a CU; at d=64 a 64-key tile already fits four.
+// Query rows per workgroup.
+template <int D>
+constexpr int kBlockMOf = 32 * kWaves * kQB<D>;
+constexpr int kBlockMMax = 32 * kWaves * 2;
+// Keys per tile for head dimension D. At d=128 a 32-key tile keeps a
+// two-block wave within 256 VGPRs (two waves per SIMD) and a workgroup at
+// 38 KiB of LDS; at d=96 a one-block wave within 128 (four per SIMD); at
+// d=64 a 64-key tile already fits four.
 template <int D>
 constexpr int kBlockN = 64;
 template <>
@@ -163,11 +179,13 @@ __global__ __launch_bounds__(kThreads, kMinBlocks<D>) void attn_fwd_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, col = lane & 31, half = lane >> 5;
 
+  constexpr int QB = kQB<D>;
+  constexpr int kBlockM = kBlockMOf<D>;
   int bh, qt;
   map_block(blockIdx.x, BH, nq, CAUSAL, bh, qt);
   const int q0 = qt * kBlockM;
-  const int qw = q0 + 32 * wave;  // first query row of this wave
-  const int qi = qw + col;        // this lane's query row
+  const int qw = q0 + 32 * QB * wave;  // first query row of this wave
+  // This lane's query row in block b is qw + 32 b + col.
 
   // Query rows live on [0, Nq), keys on [0, Nk); query i sits at key position
   // i + off (the two axes aligned at their ends; off = 0 when Nq == Nk).
@@ -180,31 +198,40 @@ __global__ __launch_bounds__(kThreads, kMinBlocks<D>) void attn_fwd_kernel(
   const rsrc_t rk = make_rsrc(K + khead, k_bytes);
   const rsrc_t rv = make_rsrc(V + khead, k_bytes);
 
-  // Q^T fragments (B operand): lane holds Q[qi][16s + 8h .. +7]; zero past N.
-  u32x4 qraw[D / 16];
+  // Q^T fragments (B operand): lane holds Q[qi][16s + 8h .. +7] of its row
+  // qi in each block; zero past N.
+  u32x4 qraw[QB][D / 16];
 #pragma unroll
-  for (int s = 0; s < D / 16; ++s)
-    qraw[s] = load16(rq, (uint32_t)(qi * D + 16 * s + 8 * half) * 2);
+  for (int b = 0; b < QB; ++b)
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s)
+      qraw[b][s] = load16(rq, (uint32_t)((qw + 32 * b + col) * D + 16 * s + 8 * half) * 2);
   // Fold the sign of the scale into Q (exact) so that c > 0 below: then a
   // masked score of -inf gets weight exp2(-inf) = 0 and the row max skips it.
   // scale == 0 makes every score 0, the same as Q == 0 with any scale.
   if (c < 0.f) {
     c = -c;
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) qraw[s] ^= 0x80008000u;
+    for (int b = 0; b < QB; ++b)
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) qraw[b][s] ^= 0x80008000u;
   } else if (c == 0.f) {
     c = 1.f;
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) qraw[s] = u32x4{0, 0, 0, 0};
-  }
-  v8 qf[D / 16];
+    for (int b = 0; b < QB; ++b)
 #pragma unroll
-  for (int s = 0; s < D / 16; ++s) qf[s] = __builtin_bit_cast(v8, qraw[s]);
+      for (int s = 0; s < D / 16; ++s) qraw[b][s] = u32x4{0, 0, 0, 0};
+  }
+  v8 qf[QB][D / 16];
+#pragma unroll
+  for (int b = 0; b < QB; ++b)
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) qf[b][s] = __builtin_bit_cast(v8, qraw[b][s]);
 
   // Keys this workgroup / this wave can see (none for rows before -off).
   const int kv_end = CAUSAL ? min(Nk, q0 + kBlockM + off) : Nk;
   const int nt = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
-  const int wave_kv_end = CAUSAL ? min(Nk, qw + 32 + off) : Nk;
+  const int wave_kv_end = CAUSAL ? min(Nk, qw + 32 * QB + off) : Nk;
 
   char* const lds = reinterpret_cast<char*>(smem);
 
@@ -269,13 +296,20 @@ __global__ __launch_bounds__(kThreads, kMinBlocks<D>) void attn_fwd_kernel(
     }
   };
 
-  f32x16 oacc[D / 32];
+  f32x16 oacc[QB][D / 32];
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
-  // Reference maximum of O and l (log2 units). It starts at -FLT_MAX, not
-  // -inf, so that a row with no visible key keeps l = 0 without NaN.
-  float m_run = -FLT_MAX;
-  float l_run = 0.f;        // this lane's share of the row sum
+  for (int b = 0; b < QB; ++b)
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) oacc[b][db] = f32x16{};
+  // Reference maximum of O and l (log2 units), per block. It starts at
+  // -FLT_MAX, not -inf, so that a row with no visible key keeps l = 0
+  // without NaN.
+  float m_run[QB], l_run[QB];  // l_run: this lane's share of the row sum
+#pragma unroll
+  for (int b = 0; b < QB; ++b) {
+    m_run[b] = -FLT_MAX;
+    l_run[b] = 0.f;
+  }
 
   // One tile: S^T, mask, running max, P, O^T += V^T P^T; then stage the next.
   auto step = [&](int t, auto stage_c) {
@@ -288,112 +322,124 @@ __global__ __launch_bounds__(kThreads, kMinBlocks<D>) void attn_fwd_kernel(
       gload(k0 + BN);
     }
 
-    if (k0 < wave_kv_end) {
+    if (k0 < wave_kv_end && qw < Nq) {
       if constexpr (kMfmaPriority<D>) __builtin_amdgcn_s_setprio(1);
-      // S^T = K * Q^T: NKB blocks of 32 keys, one MFMA chain each.
-      f32x16 sacc[NKB];
+      // S^T = K * Q^T: NKB blocks of 32 keys, one MFMA chain each per query
+      // block; each K fragment read from LDS serves every query block.
+      f32x16 sacc[QB][NKB];
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
-        sacc[kb] = f32x16{};
+#pragma unroll
+        for (int b = 0; b < QB; ++b) sacc[b][kb] = f32x16{};
 #pragma unroll
         for (int j = 0; j < D / 16; ++j) {
           const v8 a = *reinterpret_cast<const v8*>(
               lds + base + k_rd + (32 * kb * KS + 16 * j) * 2);
-          sacc[kb] = Elem<E>::mfma(a, qf[j], sacc[kb]);
+#pragma unroll
+          for (int b = 0; b < QB; ++b) sacc[b][kb] = Elem<E>::mfma(a, qf[b][j], sacc[b][kb]);
         }
       }
 
       if constexpr (kMfmaPriority<D>) __builtin_amdgcn_s_setprio(0);
       // Keys past the end and (causal) keys after the query get -inf.
       // Register i of block kb holds key k0 + 4 half + o_i. With 32 or more
-      // scores a lane (d = 32 and 64) a bit select on the sign of lim - o_i,
-      // lim being the last key the lane's query sees less k0 + 4 half:
-      // compares would hold a lane mask (two SGPRs) per score until its
-      // select, and the SGPRs spill (at d = 64 the causal kernel spilled 18
-      // SGPRs and 3 VGPRs; without them it ran 3.3% faster on causal
-      // B=8 H=16 N=2048, measured interleaved). With 16 scores a lane a
-      // compare and select per score (the bit select costs VGPRs there: at
-      // d = 96 it would cost the fourth wave per SIMD).
+      // scores a lane (d = 32 and 64, and d = 128 with two query blocks) a
+      // bit select on the sign of lim - o_i, lim being the last key the
+      // lane's query sees less k0 + 4 half: compares would hold a lane mask
+      // (two SGPRs) per score until its select, and the SGPRs spill (at
+      // d = 64 the causal kernel spilled 18 SGPRs and 3 VGPRs; without them
+      // it ran 3.3% faster on causal B=8 H=16 N=2048, measured interleaved;
+      // at d = 128 it spilled 40). With 16 scores a lane a compare and
+      // select per score (the bit select costs VGPRs there: at d = 96 it
+      // would cost the fourth wave per SIMD).
       if ((k0 + BN > Nk) || (CAUSAL && k0 + BN - 1 > qw + off)) {
-        if constexpr (NKB * 16 >= 32) {
-          const int lim = (CAUSAL ? min(Nk - 1, qi + off) : Nk - 1) - k0 - 4 * half;
 #pragma unroll
-          for (int kb = 0; kb < NKB; ++kb)
+        for (int b = 0; b < QB; ++b) {
+          const int qi = qw + 32 * b + col;
+          if constexpr (NKB * 16 * QB >= 32) {
+            const int lim = (CAUSAL ? min(Nk - 1, qi + off) : Nk - 1) - k0 - 4 * half;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int o = 32 * kb + 8 * (i >> 2) + (i & 3);
-              sacc[kb][i] = neg_inf_where((lim - o) >> 31, sacc[kb][i]);
-            }
-        } else {
+            for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-          for (int kb = 0; kb < NKB; ++kb)
+              for (int i = 0; i < 16; ++i) {
+                const int o = 32 * kb + 8 * (i >> 2) + (i & 3);
+                sacc[b][kb][i] = neg_inf_where((lim - o) >> 31, sacc[b][kb][i]);
+              }
+          } else {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int key = k0 + 32 * kb + 8 * (i >> 2) + 4 * half + (i & 3);
-              if (key >= Nk || (CAUSAL && key > qi + off)) sacc[kb][i] = -INFINITY;
-            }
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+              for (int i = 0; i < 16; ++i) {
+                const int key = k0 + 32 * kb + 8 * (i >> 2) + 4 * half + (i & 3);
+                if (key >= Nk || (CAUSAL && key > qi + off)) sacc[b][kb][i] = -INFINITY;
+              }
+          }
         }
       }
 
       // P = 2^(s*c - m_run), rounded to bf16, and its row sum (fp32).
-      v8 pb[NKB][2];
-      float tsum = 0.f;
-      auto weights = [&]() __attribute__((always_inline)) {
+      v8 pb[QB][NKB][2];
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
+      for (int b = 0; b < QB; ++b) {
+        float tsum = 0.f;
+        auto weights = [&]() __attribute__((always_inline)) {
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kb][i], c, -m_run));
-            // The sum starts at the first weight: 0 + p is not folded when
-            // signed zeros are honoured, and would cost an add per tile
-            // (+0.2% to +0.8% measured interleaved without it).
-            if (kb == 0 && i == 0)
-              tsum = p;
-            else
-              tsum += p;
-            pb[kb][i >> 3][i & 7] = (E)p;
+          for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const float p = __builtin_amdgcn_exp2f(fmaf(sacc[b][kb][i], c, -m_run[b]));
+              // The sum starts at the first weight: 0 + p is not folded when
+              // signed zeros are honoured, and would cost an add per tile
+              // (+0.2% to +0.8% measured interleaved without it).
+              if (kb == 0 && i == 0)
+                tsum = p;
+              else
+                tsum += p;
+              pb[b][kb][i >> 3][i & 7] = (E)p;
+            }
+        };
+        // Row maximum of the tile in log2 units, both lane halves combined.
+        auto tile_max = [&]() __attribute__((always_inline)) {
+          float mx = fmaxf(sacc[b][0][0], sacc[b][0][1]);
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int i = kb ? 0 : 2; i < 16; i += 2)
+              mx = fmaxf(mx, fmaxf(sacc[b][kb][i], sacc[b][kb][i + 1]));
+          return swap_halves_max(mx) * c;
+        };
+        // Move O and l to a new reference maximum.
+        auto rebase = [&](float m_new) __attribute__((always_inline)) {
+          const float alpha = __builtin_amdgcn_exp2f(m_run[b] - m_new);
+          l_run[b] *= alpha;
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db) oacc[b][db] *= alpha;
+          m_run[b] = m_new;
+        };
+        if constexpr (kSpeculativeWeights<D>) {
+          // Weights against the current reference, without the tile's own
+          // maximum. The reference moves only when this lane's share of the
+          // tile's weights exceeds kLazySum (every weight then stayed below
+          // it), and always on the first tile, where m_run = -inf: the tile's
+          // true row maximum becomes the reference and the weights are redone.
+          weights();
+          if (t == 0 || __any(tsum > kLazySum)) {
+            rebase(fmaxf(m_run[b], tile_max()));
+            weights();
           }
-      };
-      // Row maximum of the tile in log2 units, both lane halves combined.
-      auto tile_max = [&]() __attribute__((always_inline)) {
-        float mx = fmaxf(sacc[0][0], sacc[0][1]);
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int i = kb ? 0 : 2; i < 16; i += 2)
-            mx = fmaxf(mx, fmaxf(sacc[kb][i], sacc[kb][i + 1]));
-        return swap_halves_max(mx) * c;
-      };
-      // Move O and l to a new reference maximum.
-      auto rebase = [&](float m_new) __attribute__((always_inline)) {
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
-        m_run = m_new;
-      };
-      if constexpr (kSpeculativeWeights<D>) {
-        // Weights against the current reference, without the tile's own
-        // maximum. The reference moves only when this lane's share of the
-        // tile's weights exceeds kLazySum (every weight then stayed below
-        // it), and always on the first tile, where m_run = -inf: the tile's
-        // true row maximum becomes the reference and the weights are redone.
-        weights();
-        if (t == 0 || __any(tsum > kLazySum)) {
-          rebase(fmaxf(m_run, tile_max()));
+        } else {
+          // Move the reference only when the tile's row maximum exceeds it by
+          // more than kLazyMax (always on the first tile).
+          const float m_tile = tile_max();
+          if (__any(m_tile > m_run[b] + kLazyMax)) rebase(fmaxf(m_run[b], m_tile));
           weights();
         }
-      } else {
-        // Move the reference only when the tile's row maximum exceeds it by
-        // more than kLazyMax (always on the first tile).
-        const float m_tile = tile_max();
-        if (__any(m_tile > m_run + kLazyMax)) rebase(fmaxf(m_run, m_tile));
-        weights();
+        l_run[b] += tsum;
       }
-      l_run += tsum;
 
       if constexpr (kMfmaPriority<D>) __builtin_amdgcn_s_setprio(1);
-      // O^T += V^T * P^T, 16 keys per MFMA.
+      // O^T += V^T * P^T, 16 keys per MFMA; each V^T fragment serves every
+      // query block.
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -401,7 +447,8 @@ __global__ __launch_bounds__(kThreads, kMinBlocks<D>) void attn_fwd_kernel(
 #pragma unroll
           for (int db = 0; db < D / 32; ++db) {
             const v8 a = tr_operand<v8, T::VS>(lds + base, v_rd, 32 * kb + 16 * sg, 32 * db);
-            oacc[db] = Elem<E>::mfma(a, pb[kb][sg], oacc[db]);
+#pragma unroll
+            for (int b = 0; b < QB; ++b) oacc[b][db] = Elem<E>::mfma(a, pb[b][kb][sg], oacc[b][db]);
           }
         }
     }
@@ -426,26 +473,30 @@ __global__ __launch_bounds__(kThreads, kMinBlocks<D>) void attn_fwd_kernel(
 
   // Epilogue: O = acc / l (bf16), lse = (m + log2 l) * ln 2. Rows past N are
   // dropped by the buffer range check.
-  const float total = swap_halves_add(l_run);
-  // A row that saw no key (l = 0) gets O = 0 and lse = -inf.
-  const float inv = total > 0.f ? 1.0f / total : 0.f;
   const rsrc_t ro = make_rsrc(O + qhead, q_bytes);
+  const rsrc_t rl = make_rsrc(LSE + (size_t)bh * Nq, (uint32_t)Nq * 4);
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db) {
+  for (int b = 0; b < QB; ++b) {
+    const int qi = qw + 32 * b + col;
+    const float total = swap_halves_add(l_run[b]);
+    // A row that saw no key (l = 0) gets O = 0 and lse = -inf.
+    const float inv = total > 0.f ? 1.0f / total : 0.f;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      v4 o4;
+    for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) o4[e] = (E)(oacc[db][4 * r + e] * inv);
-      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, o4), ro,
-                                            (int)((qi * D + 32 * db + 8 * r + 4 * half) * 2),
-                                            0, 0);
+      for (int r = 0; r < 4; ++r) {
+        v4 o4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o4[e] = (E)(oacc[b][db][4 * r + e] * inv);
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, o4), ro,
+                                              (int)((qi * D + 32 * db + 8 * r + 4 * half) * 2),
+                                              0, 0);
+      }
     }
-  }
-  if (half == 0) {
-    const rsrc_t rl = make_rsrc(LSE + (size_t)bh * Nq, (uint32_t)Nq * 4);
-    const float lse = total > 0.f ? (m_run + log2f(total)) * kLn2 : -INFINITY;
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lse), rl, qi * 4, 0, 0);
+    if (half == 0) {
+      const float lse = total > 0.f ? (m_run[b] + log2f(total)) * kLn2 : -INFINITY;
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lse), rl, qi * 4, 0, 0);
+    }
   }
 }
 
@@ -459,6 +510,7 @@ template <int D>
 void tile_info(Shape* sh) {
   sh->lds = Tile<kLayoutD<D>, kBlockN<D>>::LDS_BYTES;
   sh->block_n = kBlockN<D>;
+  sh->block_m = kBlockMOf<D>;
 }
 
 // Sizes shared by every entry point; Nk only bounds the key tensors.
@@ -466,13 +518,9 @@ int check_sizes(int B, int H, int Nq, int Nk, int d, Shape* sh) {
   if (B < 0 || H < 0 || Nq < 0 || Nk < 0) return ATTN_ERR_SHAPE;
   if (d != 32 && d != 64 && d != 96 && d != 128 && d != 256) return ATTN_ERR_HEADDIM;
   // One head's tensors are addressed with 32-bit byte offsets (plus one tile).
-  if ((int64_t)Nq * d * 2 + (int64_t)kBlockM * d * 2 > INT32_MAX) return ATTN_ERR_SHAPE;
+  if ((int64_t)Nq * d * 2 + (int64_t)kBlockMMax * d * 2 > INT32_MAX) return ATTN_ERR_SHAPE;
   if ((int64_t)Nk * d * 2 + (int64_t)128 * d * 2 > INT32_MAX) return ATTN_ERR_SHAPE;
   if ((int64_t)B * H > INT32_MAX) return ATTN_ERR_SHAPE;
-  const int64_t nq = ((int64_t)Nq + kBlockM - 1) / kBlockM;
-  const int64_t grid = (int64_t)B * H * nq;
-  if (grid > INT32_MAX) return ATTN_ERR_SHAPE;
-  sh->grid = (int)grid;
   sh->block = kThreads;
   switch (d) {
     case 32: tile_info<32>(sh); break;
@@ -481,7 +529,10 @@ int check_sizes(int B, int H, int Nq, int Nk, int d, Shape* sh) {
     case 128: tile_info<128>(sh); break;
     default: tile_info<256>(sh); break;
   }
-  sh->block_m = kBlockM;
+  const int64_t nq = ((int64_t)Nq + sh->block_m - 1) / sh->block_m;
+  const int64_t grid = (int64_t)B * H * nq;
+  if (grid > INT32_MAX) return ATTN_ERR_SHAPE;
+  sh->grid = (int)grid;
   sh->nq = (int)nq;
   return ATTN_OK;
 }
