@@ -76,11 +76,13 @@ template <int D>
 constexpr bool kSpeculativeWeights = D >= 64;
 // Raise a wave's priority while it issues its two MFMA chains (and drop it
 // for the softmax and the staging), so that when several waves of a SIMD
-// have work the matrix pipe is fed first: +1.2-2.2% at d = 128 (measured
-// interleaved against the plain kernel); at d = 64 with weights first part
-// of the gain above; at d = 32 not kept.
+// have work the matrix pipe is fed first: +1.2-2.2% at d = 128 with one
+// query block per wave (measured interleaved against the plain kernel); at
+// d = 64 with weights first part of the gain above; at d = 32 not kept. With
+// two query blocks per wave (d = 128, two waves per SIMD) it gains nothing
+// (+0.1%, and -0.7% on the long causal shape), so it is left out there.
 template <int D>
-constexpr bool kMfmaPriority = D >= 64;
+constexpr bool kMfmaPriority = D >= 64 && D != 128;
 // Stage K and V by buffer loads that write LDS directly (no registers, no
 // LDS write instructions) instead of through registers. Timing copies that
 // drop the global loads but keep the LDS writes ran 16% faster at d = 128:
