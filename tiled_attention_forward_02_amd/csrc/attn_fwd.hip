@@ -103,21 +103,23 @@ constexpr bool kVDma = D == 64 || D == 96 || D == 128;
 // interleaved: +1.4% at d = 128, +0.9% on the long causal d = 128 shape,
 // +2.3% and +1.8% on two non-causal d = 64 shapes, +2.8% at d = 96, +1.8% at
 // d = 256, and with the bit-select mask below +1.4% on causal d = 64.
-// Workgroups per CU the register allocation must allow.
+
 // 32-query blocks per wave. At d = 128 a wave owns two blocks (64 queries):
 // every K and V^T fragment it reads from LDS then serves both, which halves
 // the LDS read traffic per FLOP, and the kernel fits in 256 VGPRs, two waves
 // per SIMD. Under the power cap that beat three one-block waves per SIMD by
-// 6.1% on B=16 H=16 N=4096 (interleaved A/B, bit-identical outputs); on the
-// long causal shape the two were level. At d = 96 (-1.1%, -6%) and d = 64
-// (-12% on the two small workloads) the fourth one-block wave per SIMD is
-// worth more, so they keep one block.
+// 3.0% and 6.1% on B=16 H=16 N=4096 on two boxes, and by 2.2% on the long
+// causal shape (interleaved A/Bs, bit-identical outputs). At d = 96 (-1.1%,
+// -6%) and d = 64 (-12% on the two small workloads) the fourth one-block
+// wave per SIMD is worth more, so they keep one block.
 template <int D>
 constexpr int kQB = D == 128 ? 2 : 1;
+// Workgroups per CU the register allocation must allow.
 template <int D>
 constexpr int kMinBlocks = kQB<D> == 2 ? 2 : D == 256 ? 1 : D == 64 ? 4 : D >= 96 ? 3 : 2;
 
-// Query rows per workgroup.
+// Query rows per workgroup, and the largest of them (the 32-bit offset
+// check on Nq allows for one workgroup's rows past the end).
 template <int D>
 constexpr int kBlockMOf = 32 * kWaves * kQB<D>;
 constexpr int kBlockMMax = 32 * kWaves * 2;
