@@ -308,3 +308,17 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
                  lambda: mi.attn_strerror(0), lambda: mi.attn_fwd_launch_shape(1, 1, 8, 64)):
         with pytest.raises(ImportError):
             call()
+
+
+@pytest.mark.parametrize("B,H,N,rows", [(16, 16, 4096, 512), (1, 32, 16384, 512),
+                                        (2, 16, 4096, 256), (4, 16, 1024, 128),
+                                        (1, 1, 128, 128)])
+def test_launch_shape_d128_follows_the_grid(lib, B, H, N, rows):
+    # d = 128 takes the biggest workgroup (512, 256 or 128 query rows) whose grid
+    # still gives each of the 256 CUs two workgroups' worth of rows
+    s = mi.attn_fwd_launch_shape(B, H, N, 128, False)
+    assert s["block_m"] == rows
+    assert s["block"] == (512 if rows == 512 else 256)
+    assert s["grid"] == B * H * ((N + rows - 1) // rows)
+    # other head dims keep 128 rows and four waves
+    assert mi.attn_fwd_launch_shape(B, H, N, 64, False)["block_m"] == 128

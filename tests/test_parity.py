@@ -472,3 +472,44 @@ def test_ex_long_sampled(d, N, causal, dt):
         o_ref, lse_ref = attend_head(q64[0, h, rows], k64[0, h], v64[0, h], inp["scale"],
                                      causal, q_pos=rows)
         check(o[0, h, rows], lse[0, h, rows], o_ref, lse_ref, f"head {h}")
+
+
+# d = 128 picks its workgroup shape from the grid size: 512 query rows a
+# workgroup (two blocks of 32 a wave, eight waves) when the grid still gives
+# each CU two workgroups' worth, else 256 (two blocks, four waves), else 128
+# (one block, four waves). Each case below lands on one shape, with ragged
+# lengths and (causal) Nq != Nk, checked on sampled rows of a few heads.
+SHAPES_128 = [
+    # (B, H, Nq, Nk, causal, rows per workgroup)
+    (8, 16, 4000, 4000, False, 512),
+    (8, 16, 4000, 4000, True, 512),
+    (8, 16, 3000, 4100, True, 512),
+    (2, 16, 4000, 4000, False, 256),
+    (2, 16, 4000, 4000, True, 256),
+    (2, 16, 3900, 1500, True, 256),
+    (1, 16, 4000, 4000, True, 128),
+]
+
+
+@pytest.mark.parametrize("B,H,Nq,Nk,causal,rows", SHAPES_128)
+def test_d128_workgroup_shapes(B, H, Nq, Nk, causal, rows):
+    announce(f"d=128 shapes B={B} H={H} Nq={Nq} Nk={Nk} causal={causal} rows={rows}")
+    assert mi.attn_fwd_launch_shape(B, H, Nq, 128, causal)["block_m"] == rows
+    qi = make_inputs(WORKLOADS[3], B=B, H=H, N=Nq, d=128, seed=8100 + Nq + B)
+    ki = qi if Nk == Nq else make_inputs(WORKLOADS[3], B=B, H=H, N=Nk, d=128, seed=8200 + Nk)
+    dev = torch.device("cuda:0")
+    o, lse = mi.attn_fwd_cross(qi["q"].to(dev), ki["k"].to(dev), ki["v"].to(dev),
+                               scale=qi["scale"], causal=causal)
+    torch.cuda.synchronize()
+    o, lse = o.float().cpu().numpy(), lse.cpu().numpy()
+    rng = np.random.default_rng(Nq + Nk + B)
+    # the first and last rows, rows on both sides of workgroup and wave-block
+    # edges, and random ones
+    edges = [0, 31, 32, 63, 64, rows - 1, rows, 2 * rows - 1, Nq - rows, Nq - 33, Nq - 1]
+    sample = np.unique(np.clip(np.concatenate([edges, rng.integers(0, Nq, 30)]), 0, Nq - 1))
+    pos = sample + (Nk - Nq)
+    for b, h in ((0, 0), (B // 2, H // 3), (B - 1, H - 1)):
+        o_ref, lse_ref = attend_head(as64(qi["q"][b, h, sample]), as64(ki["k"][b, h]),
+                                     as64(ki["v"][b, h]), qi["scale"], causal, q_pos=pos)
+        check_with_empty_rows(o[b, h, sample], lse[b, h, sample], o_ref, lse_ref,
+                              f"head ({b},{h})")

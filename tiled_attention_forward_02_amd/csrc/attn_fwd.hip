@@ -81,8 +81,8 @@ constexpr bool kSpeculativeWeights = D >= 64;
 // d = 64 with weights first part of the gain above; at d = 32 not kept. With
 // two query blocks per wave (d = 128, two waves per SIMD) it gains nothing
 // (+0.1%, and -0.7% on the long causal shape), so it is left out there.
-template <int D>
-constexpr bool kMfmaPriority = D >= 64 && D != 128;
+template <int D, int QB>
+constexpr bool kMfmaPriority = D >= 64 && QB == 1;
 // Stage K and V by buffer loads that write LDS directly (no registers, no
 // LDS write instructions) instead of through registers. Timing copies that
 // drop the global loads but keep the LDS writes ran 16% faster at d = 128:
@@ -104,25 +104,27 @@ constexpr bool kVDma = D == 64 || D == 96 || D == 128;
 // +2.3% and +1.8% on two non-causal d = 64 shapes, +2.8% at d = 96, +1.8% at
 // d = 256, and with the bit-select mask below +1.4% on causal d = 64.
 
-// 32-query blocks per wave. At d = 128 a wave owns two blocks (64 queries):
-// every K and V^T fragment it reads from LDS then serves both, which halves
-// the LDS read traffic per FLOP, and the kernel fits in 256 VGPRs, two waves
-// per SIMD. Under the power cap that beat three one-block waves per SIMD by
-// 3.0% and 6.1% on B=16 H=16 N=4096 on two boxes, and by 2.2% on the long
-// causal shape (interleaved A/Bs, bit-identical outputs). At d = 96 (-1.1%,
-// -6%) and d = 64 (-12% on the two small workloads) the fourth one-block
-// wave per SIMD is worth more, so they keep one block.
-template <int D>
-constexpr int kQB = D == 128 ? 2 : 1;
+// Workgroup shapes: QB 32-query blocks per wave, NW waves per workgroup.
+// d = 128 has three, chosen at launch by the size of the grid:
+// - QB = 2, NW = 8 (512 rows a workgroup, one per CU, two waves per SIMD);
+// - QB = 2, NW = 4 (256 rows, two per CU, two waves per SIMD);
+// - QB = 1, NW = 4 (128 rows, three per CU, three waves per SIMD).
+// With two blocks a wave, every K and V^T fragment it reads from LDS serves
+// both, which halves the LDS read traffic per FLOP; the kernel then fits in
+// 256 VGPRs, two waves per SIMD. Under the power cap that beat three
+// one-block waves per SIMD by 3.0% and 6.1% on B=16 H=16 N=4096 on two boxes,
+// and by 2.2% on the long causal shape. Eight waves a workgroup then halve
+// the HBM -> LDS staging per FLOP again: a further +2.0% and +0.9% (all
+// interleaved A/Bs, bit-identical outputs). Bigger workgroups mean fewer of
+// them, so small grids keep the smaller shapes. At d = 96 (-1.1%, -6%) and
+// d = 64 (-12% on the two small workloads) two blocks lost to the fourth
+// one-block wave per SIMD, so every other d runs QB = 1, NW = 4.
 // Workgroups per CU the register allocation must allow.
-template <int D>
-constexpr int kMinBlocks = kQB<D> == 2 ? 2 : D == 256 ? 1 : D == 64 ? 4 : D >= 96 ? 3 : 2;
-
-// Query rows per workgroup, and the largest of them (the 32-bit offset
-// check on Nq allows for one workgroup's rows past the end).
-template <int D>
-constexpr int kBlockMOf = 32 * kWaves * kQB<D>;
-constexpr int kBlockMMax = 32 * kWaves * 2;
+template <int D, int QB, int NW>
+constexpr int kMinBlocks = QB == 2 ? 8 / NW : D == 256 ? 1 : D == 64 ? 4 : D >= 96 ? 3 : 2;
+// The most query rows a workgroup has (the 32-bit offset check on Nq allows
+// for one workgroup's rows past the end).
+constexpr int kBlockMMax = 32 * 8 * 2;
 // Keys per tile for head dimension D. At d=128 a 32-key tile keeps a
 // two-block wave within 256 VGPRs (two waves per SIMD) and a workgroup at
 // 38 KiB of LDS; at d=96 a one-block wave within 128 (four per SIMD); at
@@ -145,7 +147,7 @@ template <int D>
 constexpr int kLayoutD = D == 96 ? 128 : D;
 
 // Per head dimension D and tile width BN: the key tile and its LDS layout.
-template <int D, int BN_>
+template <int D, int BN_, int NW = kWaves>
 struct Tile {
   static constexpr int BN = BN_;
   static constexpr int NKB = BN / 32;            // 32-key MFMA blocks per tile
@@ -157,19 +159,21 @@ struct Tile {
   static constexpr int VS = tr_pitch<D>();       // V row pitch in LDS
   static constexpr int V_ELEMS = BN * VS;        // one V tile, row-major
   static constexpr int CPR = D / 8;              // 16-byte chunks per row
-  static constexpr int KPT = BN * CPR / kThreads;  // rows each thread stages (4 or 2)
+  // Rows each thread stages through registers (d = 32 and the V tile at
+  // d = 256, both with four waves; the other shapes stage by DMA).
+  static constexpr int KPT = BN * CPR / (64 * NW) > 0 ? BN * CPR / (64 * NW) : 1;
   static constexpr int STAGE = K_SPAN + V_ELEMS;
   static constexpr int LDS_ELEMS = 2 * STAGE;
   static constexpr int LDS_BYTES = 2 * LDS_ELEMS;
-  static_assert(KPT == 2 || KPT == 4, "staging layout");
+  static_assert(NW != kWaves || KPT == 2 || KPT == 4, "staging layout");
 };
 
-template <typename E, int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, kMinBlocks<D>) void attn_fwd_kernel(
+template <typename E, int D, bool CAUSAL, int QB, int NW>
+__global__ __launch_bounds__(64 * NW, (kMinBlocks<D, QB, NW>)) void attn_fwd_kernel(
     const E* __restrict__ Q, const E* __restrict__ K,
     const E* __restrict__ V, E* __restrict__ O,
     float* __restrict__ LSE, int BH, int Nq, int Nk, int nq, float c) {
-  using T = Tile<kLayoutD<D>, kBlockN<D>>;
+  using T = Tile<kLayoutD<D>, kBlockN<D>, NW>;
   constexpr int BN = T::BN, KS = T::KS, CPR = T::CPR, KPT = T::KPT, NKB = T::NKB;
   // Chunks of a row that hold data (all but the layout's padding at d = 96).
   constexpr int CPR_DATA = D / 8;
@@ -183,8 +187,7 @@ __global__ __launch_bounds__(kThreads, kMinBlocks<D>) void attn_fwd_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, col = lane & 31, half = lane >> 5;
 
-  constexpr int QB = kQB<D>;
-  constexpr int kBlockM = kBlockMOf<D>;
+  constexpr int kBlockM = 32 * NW * QB;
   int bh, qt;
   map_block(blockIdx.x, BH, nq, CAUSAL, bh, qt);
   const int q0 = qt * kBlockM;
@@ -241,8 +244,8 @@ __global__ __launch_bounds__(kThreads, kMinBlocks<D>) void attn_fwd_kernel(
 
   // Staging by DMA (DmaTile): K and V tiles straight from HBM into LDS, no
   // registers; the K tile's LDS span is rounded up to 1024 bytes for it.
-  typedef DmaTile<D, BN, KS> KDma;
-  typedef DmaTile<D, BN, T::VS> VDma;
+  typedef DmaTile<D, BN, KS, NW> KDma;
+  typedef DmaTile<D, BN, T::VS, NW> VDma;
   static_assert(KDma::SPAN == T::K_SPAN * 2, "K DMA span is the K tile's LDS span");
   static_assert(!kVDma<D> || VDma::SPAN == T::V_ELEMS * 2, "V DMA covers the V tile exactly");
   lds_char* const lds3 = to_lds(smem);
@@ -327,7 +330,7 @@ __global__ __launch_bounds__(kThreads, kMinBlocks<D>) void attn_fwd_kernel(
     }
 
     if (k0 < wave_kv_end && qw < Nq) {
-      if constexpr (kMfmaPriority<D>) __builtin_amdgcn_s_setprio(1);
+      if constexpr ((kMfmaPriority<D, QB>)) __builtin_amdgcn_s_setprio(1);
       // S^T = K * Q^T: NKB blocks of 32 keys, one MFMA chain each per query
       // block; each K fragment read from LDS serves every query block.
       f32x16 sacc[QB][NKB];
@@ -344,7 +347,7 @@ __global__ __launch_bounds__(kThreads, kMinBlocks<D>) void attn_fwd_kernel(
         }
       }
 
-      if constexpr (kMfmaPriority<D>) __builtin_amdgcn_s_setprio(0);
+      if constexpr ((kMfmaPriority<D, QB>)) __builtin_amdgcn_s_setprio(0);
       // Keys past the end and (causal) keys after the query get -inf.
       // Register i of block kb holds key k0 + 4 half + o_i. With 32 or more
       // scores a lane (d = 32 and 64, and d = 128 with two query blocks) a
@@ -441,7 +444,7 @@ __global__ __launch_bounds__(kThreads, kMinBlocks<D>) void attn_fwd_kernel(
         l_run[b] += tsum;
       }
 
-      if constexpr (kMfmaPriority<D>) __builtin_amdgcn_s_setprio(1);
+      if constexpr ((kMfmaPriority<D, QB>)) __builtin_amdgcn_s_setprio(1);
       // O^T += V^T * P^T, 16 keys per MFMA; each V^T fragment serves every
       // query block.
 #pragma unroll
@@ -457,7 +460,7 @@ __global__ __launch_bounds__(kThreads, kMinBlocks<D>) void attn_fwd_kernel(
         }
     }
 
-    if constexpr (kMfmaPriority<D>) __builtin_amdgcn_s_setprio(0);
+    if constexpr ((kMfmaPriority<D, QB>)) __builtin_amdgcn_s_setprio(0);
     if (has_next) lds_store(std::integral_constant<int, stage ^ 1>{});
     // DMA form: the next tile's K lands in LDS with no instruction of this
     // wave writing it; wait for the loads before the barrier.
@@ -508,13 +511,28 @@ __global__ __launch_bounds__(kThreads, kMinBlocks<D>) void attn_fwd_kernel(
 
 struct Shape {
   int grid, block, lds, block_m, block_n, nq;
+  int qb, nw;  // 32-query blocks per wave, waves per workgroup
 };
 
 template <int D>
 void tile_info(Shape* sh) {
-  sh->lds = Tile<kLayoutD<D>, kBlockN<D>>::LDS_BYTES;
+  sh->lds = Tile<kLayoutD<D>, kBlockN<D>>::LDS_BYTES;  // the same for every NW
   sh->block_n = kBlockN<D>;
-  sh->block_m = kBlockMOf<D>;
+}
+
+// The workgroup shape at d = 128: the largest whose grid still gives every CU
+// two workgroups' worth of rows (512-row workgroups: two rounds of one per
+// CU; 256-row ones: one round of two per CU), else 128 rows.
+void pick_shape_128(int64_t BH, int Nq, int* qb, int* nw) {
+  constexpr int64_t kCUs = 256;
+  auto grid = [&](int rows) { return BH * (((int64_t)Nq + rows - 1) / rows); };
+  if (grid(512) >= 2 * kCUs) {
+    *qb = 2, *nw = 8;
+  } else if (grid(256) >= 2 * kCUs) {
+    *qb = 2, *nw = 4;
+  } else {
+    *qb = 1, *nw = 4;
+  }
 }
 
 // Sizes shared by every entry point; Nk only bounds the key tensors.
@@ -525,7 +543,6 @@ int check_sizes(int B, int H, int Nq, int Nk, int d, Shape* sh) {
   if ((int64_t)Nq * d * 2 + (int64_t)kBlockMMax * d * 2 > INT32_MAX) return ATTN_ERR_SHAPE;
   if ((int64_t)Nk * d * 2 + (int64_t)128 * d * 2 > INT32_MAX) return ATTN_ERR_SHAPE;
   if ((int64_t)B * H > INT32_MAX) return ATTN_ERR_SHAPE;
-  sh->block = kThreads;
   switch (d) {
     case 32: tile_info<32>(sh); break;
     case 64: tile_info<64>(sh); break;
@@ -533,6 +550,10 @@ int check_sizes(int B, int H, int Nq, int Nk, int d, Shape* sh) {
     case 128: tile_info<128>(sh); break;
     default: tile_info<256>(sh); break;
   }
+  sh->qb = 1, sh->nw = kWaves;
+  if (d == 128) pick_shape_128((int64_t)B * H, Nq, &sh->qb, &sh->nw);
+  sh->block = 64 * sh->nw;
+  sh->block_m = 32 * sh->nw * sh->qb;
   const int64_t nq = ((int64_t)Nq + sh->block_m - 1) / sh->block_m;
   const int64_t grid = (int64_t)B * H * nq;
   if (grid > INT32_MAX) return ATTN_ERR_SHAPE;
@@ -556,7 +577,7 @@ struct Args {
   hipStream_t stream;
 };
 
-template <typename E, int D, bool CAUSAL>
+template <typename E, int D, bool CAUSAL, int QB, int NW>
 hipError_t launch(const Shape& sh, const Args& a) {
   const E* qp = static_cast<const E*>(a.q);
   const E* kp = static_cast<const E*>(a.k);
@@ -566,18 +587,29 @@ hipError_t launch(const Shape& sh, const Args& a) {
   int BH = a.BH, Nq = a.Nq, Nk = a.Nk, nq = sh.nq;
   float c = a.c;
   void* args[] = {&qp, &kp, &vp, &op, &lp, &BH, &Nq, &Nk, &nq, &c};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&attn_fwd_kernel<E, D, CAUSAL>),
+  return hipLaunchKernel(reinterpret_cast<const void*>(&attn_fwd_kernel<E, D, CAUSAL, QB, NW>),
                          dim3(sh.grid), dim3(sh.block), args, 0, a.stream);
+}
+
+template <typename E, int D, bool CAUSAL>
+hipError_t launch_shape(const Shape& sh, const Args& a) {
+  if constexpr (D == 128) {
+    if (sh.qb == 2 && sh.nw == 8) return launch<E, D, CAUSAL, 2, 8>(sh, a);
+    if (sh.qb == 2) return launch<E, D, CAUSAL, 2, 4>(sh, a);
+  }
+  return launch<E, D, CAUSAL, 1, kWaves>(sh, a);
 }
 
 template <typename E>
 hipError_t launch_type(const Shape& sh, const Args& a, int d, bool causal) {
   switch (d) {
-    case 32: return causal ? launch<E, 32, true>(sh, a) : launch<E, 32, false>(sh, a);
-    case 64: return causal ? launch<E, 64, true>(sh, a) : launch<E, 64, false>(sh, a);
-    case 96: return causal ? launch<E, 96, true>(sh, a) : launch<E, 96, false>(sh, a);
-    case 128: return causal ? launch<E, 128, true>(sh, a) : launch<E, 128, false>(sh, a);
-    default: return causal ? launch<E, 256, true>(sh, a) : launch<E, 256, false>(sh, a);
+    case 32: return causal ? launch_shape<E, 32, true>(sh, a) : launch_shape<E, 32, false>(sh, a);
+    case 64: return causal ? launch_shape<E, 64, true>(sh, a) : launch_shape<E, 64, false>(sh, a);
+    case 96: return causal ? launch_shape<E, 96, true>(sh, a) : launch_shape<E, 96, false>(sh, a);
+    case 128:
+      return causal ? launch_shape<E, 128, true>(sh, a) : launch_shape<E, 128, false>(sh, a);
+    default:
+      return causal ? launch_shape<E, 256, true>(sh, a) : launch_shape<E, 256, false>(sh, a);
   }
 }
 

@@ -120,24 +120,24 @@ __device__ __forceinline__ void load16_lds(rsrc_t r, lds_char* lds_base, uint32_
 // LDS DMA of one row-major tile: the first BR rows of a [*, D] tensor (16-bit
 // elements) that a buffer resource starts at, into BR rows of PITCH
 // elements, PITCH / 8 16-byte slots a row of which D / 8 hold data.
-// Instruction u of the tile (u = wave, wave + kWaves, ...; whether u exists
+// Instruction u of the tile (u = wave, wave + W, ...; W waves; whether u exists
 // is a uniform branch) writes slots 64 u .. 64 u + 63, lane l slot
 // 64 u + l; lanes of pad slots, of chunks past the data and past the tile
 // get an offset beyond any buffer (zeros, no fetch). The instructions write
 // SPAN bytes from the tile's start, a multiple of 1024 that the caller's
 // layout reserves.
-template <int D, int BR, int PITCH>
+template <int D, int BR, int PITCH, int W = kWaves>
 struct DmaTile {
   static constexpr int SLOTS = PITCH / 8;
   static constexpr int NINSTR = (BR * SLOTS + 63) / 64;
-  static constexpr int NW = (NINSTR + kWaves - 1) / kWaves;  // per wave, at most
+  static constexpr int NW = (NINSTR + W - 1) / W;  // per wave, at most
   static constexpr int SPAN = NINSTR * 1024;
   static constexpr uint32_t kNoFetch = 0x80000000u;  // > any head's bytes
   uint32_t off[NW];
   __device__ __forceinline__ DmaTile(int wave, int lane) {
 #pragma unroll
     for (int i = 0; i < NW; ++i) {
-      const int slot = 64 * (wave + kWaves * i) + lane;
+      const int slot = 64 * (wave + W * i) + lane;
       const int row = slot / SLOTS, ch = slot % SLOTS;
       off[i] = row < BR && ch < D / 8 ? (uint32_t)(row * D + 8 * ch) * 2 : kNoFetch;
     }
@@ -148,7 +148,7 @@ struct DmaTile {
   __device__ __forceinline__ void issue(rsrc_t r_tile, lds_char* tile, int wave) const {
 #pragma unroll
     for (int i = 0; i < NW; ++i) {
-      const int u = wave + kWaves * i;
+      const int u = wave + W * i;
       if (u < NINSTR) load16_lds(r_tile, tile + 1024 * u, off[i]);
     }
   }
