@@ -322,3 +322,15 @@ def test_launch_shape_d128_follows_the_grid(lib, B, H, N, rows):
     assert s["grid"] == B * H * ((N + rows - 1) // rows)
     # other head dims keep 128 rows and four waves
     assert mi.attn_fwd_launch_shape(B, H, N, 64, False)["block_m"] == 128
+
+
+@pytest.mark.parametrize("B,H,N,rows", [(16, 16, 4096, 256), (1, 32, 16384, 256),
+                                        (4, 16, 4000, 256), (2, 16, 4000, 128),
+                                        (4, 16, 1024, 128)])
+def test_launch_shape_d96_follows_the_grid(lib, B, H, N, rows):
+    # d = 96 takes eight-wave, 256-row workgroups when the grid gives two full
+    # rounds of two per CU, else four-wave, 128-row ones
+    s = mi.attn_fwd_launch_shape(B, H, N, 96, True)
+    assert s["block_m"] == rows
+    assert s["block"] == (512 if rows == 256 else 256)
+    assert s["grid"] == B * H * ((N + rows - 1) // rows)

@@ -477,26 +477,33 @@ def test_ex_long_sampled(d, N, causal, dt):
 # d = 128 picks its workgroup shape from the grid size: 512 query rows a
 # workgroup (two blocks of 32 a wave, eight waves) when the grid still gives
 # each CU two workgroups' worth, else 256 (two blocks, four waves), else 128
-# (one block, four waves). Each case below lands on one shape, with ragged
-# lengths and (causal) Nq != Nk, checked on sampled rows of a few heads.
-SHAPES_128 = [
-    # (B, H, Nq, Nk, causal, rows per workgroup)
-    (8, 16, 4000, 4000, False, 512),
-    (8, 16, 4000, 4000, True, 512),
-    (8, 16, 3000, 4100, True, 512),
-    (2, 16, 4000, 4000, False, 256),
-    (2, 16, 4000, 4000, True, 256),
-    (2, 16, 3900, 1500, True, 256),
-    (1, 16, 4000, 4000, True, 128),
+# (one block, four waves). d = 96 takes eight one-block waves (256 rows) on
+# grids of two full rounds, else four. Each case below lands on one shape,
+# with ragged lengths and (causal) Nq != Nk, checked on sampled rows of a few
+# heads.
+SHAPES = [
+    # (d, B, H, Nq, Nk, causal, rows per workgroup)
+    (128, 8, 16, 4000, 4000, False, 512),
+    (128, 8, 16, 4000, 4000, True, 512),
+    (128, 8, 16, 3000, 4100, True, 512),
+    (128, 2, 16, 4000, 4000, False, 256),
+    (128, 2, 16, 4000, 4000, True, 256),
+    (128, 2, 16, 3900, 1500, True, 256),
+    (128, 1, 16, 4000, 4000, True, 128),
+    (96, 4, 16, 4000, 4000, False, 256),
+    (96, 4, 16, 4000, 4000, True, 256),
+    (96, 6, 16, 3000, 4100, True, 256),
+    (96, 2, 16, 4000, 4000, True, 128),
 ]
 
 
-@pytest.mark.parametrize("B,H,Nq,Nk,causal,rows", SHAPES_128)
-def test_d128_workgroup_shapes(B, H, Nq, Nk, causal, rows):
-    announce(f"d=128 shapes B={B} H={H} Nq={Nq} Nk={Nk} causal={causal} rows={rows}")
-    assert mi.attn_fwd_launch_shape(B, H, Nq, 128, causal)["block_m"] == rows
-    qi = make_inputs(WORKLOADS[3], B=B, H=H, N=Nq, d=128, seed=8100 + Nq + B)
-    ki = qi if Nk == Nq else make_inputs(WORKLOADS[3], B=B, H=H, N=Nk, d=128, seed=8200 + Nk)
+@pytest.mark.parametrize("d,B,H,Nq,Nk,causal,rows", SHAPES)
+def test_workgroup_shapes(d, B, H, Nq, Nk, causal, rows):
+    announce(f"shapes d={d} B={B} H={H} Nq={Nq} Nk={Nk} causal={causal} rows={rows}")
+    assert mi.attn_fwd_launch_shape(B, H, Nq, d, causal)["block_m"] == rows
+    qi = make_inputs(WORKLOADS[3], B=B, H=H, N=Nq, d=d, seed=8100 + Nq + B + d)
+    ki = qi if Nk == Nq else make_inputs(WORKLOADS[3], B=B, H=H, N=Nk, d=d,
+                                         seed=8200 + Nk + d)
     dev = torch.device("cuda:0")
     o, lse = mi.attn_fwd_cross(qi["q"].to(dev), ki["k"].to(dev), ki["v"].to(dev),
                                scale=qi["scale"], causal=causal)

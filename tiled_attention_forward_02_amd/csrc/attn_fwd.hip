@@ -105,7 +105,12 @@ constexpr bool kVDma = D == 64 || D == 96 || D == 128;
 // d = 256, and with the bit-select mask below +1.4% on causal d = 64.
 
 // Workgroup shapes: QB 32-query blocks per wave, NW waves per workgroup.
-// d = 128 has three, chosen at launch by the size of the grid:
+// d = 96 has two, chosen at launch by the size of the grid: eight waves of
+// one block (256 rows; two workgroups per CU, four waves per SIMD) on big
+// grids, which halves the HBM -> LDS staging per FLOP (+2.7% on B=16 H=16
+// N=4096, +3.4% on the long causal shape, interleaved), else four waves. At
+// d = 64 eight waves gained +0.5% on big grids and lost 2.6-2.8% on the two
+// small workloads, so d = 64 keeps four. d = 128 has three:
 // - QB = 2, NW = 8 (512 rows a workgroup, one per CU, two waves per SIMD);
 // - QB = 2, NW = 4 (256 rows, two per CU, two waves per SIMD);
 // - QB = 1, NW = 4 (128 rows, three per CU, three waves per SIMD).
@@ -121,7 +126,8 @@ constexpr bool kVDma = D == 64 || D == 96 || D == 128;
 // one-block wave per SIMD, so every other d runs QB = 1, NW = 4.
 // Workgroups per CU the register allocation must allow.
 template <int D, int QB, int NW>
-constexpr int kMinBlocks = QB == 2 ? 8 / NW : D == 256 ? 1 : D == 64 ? 4 : D >= 96 ? 3 : 2;
+constexpr int kMinBlocks =
+    QB == 2 ? 8 / NW : (D == 256 ? 1 : D == 64 ? 4 : D >= 96 ? 3 : 2) * kWaves / NW;
 // The most query rows a workgroup has (the 32-bit offset check on Nq allows
 // for one workgroup's rows past the end).
 constexpr int kBlockMMax = 32 * 8 * 2;
@@ -520,11 +526,12 @@ void tile_info(Shape* sh) {
   sh->block_n = kBlockN<D>;
 }
 
+constexpr int64_t kCUs = 256;  // gfx950 parts have 256 CUs
+
 // The workgroup shape at d = 128: the largest whose grid still gives every CU
 // two workgroups' worth of rows (512-row workgroups: two rounds of one per
 // CU; 256-row ones: one round of two per CU), else 128 rows.
 void pick_shape_128(int64_t BH, int Nq, int* qb, int* nw) {
-  constexpr int64_t kCUs = 256;
   auto grid = [&](int rows) { return BH * (((int64_t)Nq + rows - 1) / rows); };
   if (grid(512) >= 2 * kCUs) {
     *qb = 2, *nw = 8;
@@ -533,6 +540,12 @@ void pick_shape_128(int64_t BH, int Nq, int* qb, int* nw) {
   } else {
     *qb = 1, *nw = 4;
   }
+}
+
+// d = 96: eight-wave workgroups (256 rows) when the grid gives two full
+// rounds of two per CU, else four waves.
+int pick_waves_96(int64_t BH, int Nq) {
+  return BH * (((int64_t)Nq + 255) / 256) >= 4 * kCUs ? 8 : 4;
 }
 
 // Sizes shared by every entry point; Nk only bounds the key tensors.
@@ -552,6 +565,7 @@ int check_sizes(int B, int H, int Nq, int Nk, int d, Shape* sh) {
   }
   sh->qb = 1, sh->nw = kWaves;
   if (d == 128) pick_shape_128((int64_t)B * H, Nq, &sh->qb, &sh->nw);
+  if (d == 96) sh->nw = pick_waves_96((int64_t)B * H, Nq);
   sh->block = 64 * sh->nw;
   sh->block_m = 32 * sh->nw * sh->qb;
   const int64_t nq = ((int64_t)Nq + sh->block_m - 1) / sh->block_m;
@@ -593,6 +607,9 @@ hipError_t launch(const Shape& sh, const Args& a) {
 
 template <typename E, int D, bool CAUSAL>
 hipError_t launch_shape(const Shape& sh, const Args& a) {
+  if constexpr (D == 96) {
+    if (sh.nw == 8) return launch<E, D, CAUSAL, 1, 8>(sh, a);
+  }
   if constexpr (D == 128) {
     if (sh.qb == 2 && sh.nw == 8) return launch<E, D, CAUSAL, 2, 8>(sh, a);
     if (sh.qb == 2) return launch<E, D, CAUSAL, 2, 4>(sh, a);
