@@ -482,31 +482,34 @@ def test_ex_long_sampled(d, N, causal, dt):
 # with ragged lengths and (causal) Nq != Nk, checked on sampled rows of a few
 # heads.
 SHAPES = [
-    # (d, B, H, Nq, Nk, causal, rows per workgroup)
-    (128, 8, 16, 4000, 4000, False, 512),
-    (128, 8, 16, 4000, 4000, True, 512),
-    (128, 8, 16, 3000, 4100, True, 512),
-    (128, 2, 16, 4000, 4000, False, 256),
-    (128, 2, 16, 4000, 4000, True, 256),
-    (128, 2, 16, 3900, 1500, True, 256),
-    (128, 1, 16, 4000, 4000, True, 128),
-    (96, 4, 16, 4000, 4000, False, 256),
-    (96, 4, 16, 4000, 4000, True, 256),
-    (96, 6, 16, 3000, 4100, True, 256),
-    (96, 2, 16, 4000, 4000, True, 128),
+    # (d, B, H, Nq, Nk, causal, rows per workgroup, element type)
+    (128, 8, 16, 4000, 4000, False, 512, "bf16"),
+    (128, 8, 16, 4000, 4000, True, 512, "bf16"),
+    (128, 8, 16, 3000, 4100, True, 512, "bf16"),
+    (128, 8, 16, 4000, 4000, True, 512, "f16"),
+    (128, 2, 16, 4000, 4000, False, 256, "bf16"),
+    (128, 2, 16, 4000, 4000, True, 256, "bf16"),
+    (128, 2, 16, 3900, 1500, True, 256, "bf16"),
+    (128, 1, 16, 4000, 4000, True, 128, "bf16"),
+    (96, 4, 16, 4000, 4000, False, 256, "bf16"),
+    (96, 4, 16, 4000, 4000, True, 256, "bf16"),
+    (96, 6, 16, 3000, 4100, True, 256, "bf16"),
+    (96, 4, 16, 4000, 4000, False, 256, "f16"),
+    (96, 2, 16, 4000, 4000, True, 128, "bf16"),
 ]
 
 
-@pytest.mark.parametrize("d,B,H,Nq,Nk,causal,rows", SHAPES)
-def test_workgroup_shapes(d, B, H, Nq, Nk, causal, rows):
-    announce(f"shapes d={d} B={B} H={H} Nq={Nq} Nk={Nk} causal={causal} rows={rows}")
+@pytest.mark.parametrize("d,B,H,Nq,Nk,causal,rows,dt", SHAPES)
+def test_workgroup_shapes(d, B, H, Nq, Nk, causal, rows, dt):
+    announce(f"shapes d={d} B={B} H={H} Nq={Nq} Nk={Nk} causal={causal} rows={rows} {dt}")
     assert mi.attn_fwd_launch_shape(B, H, Nq, d, causal)["block_m"] == rows
-    qi = make_inputs(WORKLOADS[3], B=B, H=H, N=Nq, d=d, seed=8100 + Nq + B + d)
+    qi = make_inputs(WORKLOADS[3], B=B, H=H, N=Nq, d=d, seed=8100 + Nq + B + d,
+                     dtype=DTYPES[dt])
     ki = qi if Nk == Nq else make_inputs(WORKLOADS[3], B=B, H=H, N=Nk, d=d,
-                                         seed=8200 + Nk + d)
+                                         seed=8200 + Nk + d, dtype=DTYPES[dt])
     dev = torch.device("cuda:0")
-    o, lse = mi.attn_fwd_cross(qi["q"].to(dev), ki["k"].to(dev), ki["v"].to(dev),
-                               scale=qi["scale"], causal=causal)
+    o, lse = mi.attn_fwd_ex(qi["q"].to(dev), ki["k"].to(dev), ki["v"].to(dev),
+                            scale=qi["scale"], causal=causal)
     torch.cuda.synchronize()
     o, lse = o.float().cpu().numpy(), lse.cpu().numpy()
     rng = np.random.default_rng(Nq + Nk + B)
