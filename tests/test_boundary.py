@@ -334,3 +334,14 @@ def test_launch_shape_d96_follows_the_grid(lib, B, H, N, rows):
     assert s["block_m"] == rows
     assert s["block"] == (512 if rows == 256 else 256)
     assert s["grid"] == B * H * ((N + rows - 1) // rows)
+
+
+@pytest.mark.parametrize("B,H,N,rows", [(16, 16, 4096, 256), (1, 32, 16384, 256),
+                                        (2, 16, 4000, 256), (1, 16, 4000, 128)])
+def test_launch_shape_d256_follows_the_grid(lib, B, H, N, rows):
+    # d = 256 takes eight-wave, 256-row workgroups when the grid gives two full
+    # rounds of one per CU, else four-wave, 128-row ones
+    s = mi.attn_fwd_launch_shape(B, H, N, 256, False)
+    assert s["block_m"] == rows
+    assert s["block"] == (512 if rows == 256 else 256)
+    assert s["grid"] == B * H * ((N + rows - 1) // rows)

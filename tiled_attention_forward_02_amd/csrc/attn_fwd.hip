@@ -15,8 +15,8 @@
 // holds waves of different workgroups whose softmax (VALU) and matrix (MFMA)
 // phases interleave. Keys and values
 // stream through LDS in tiles of 32 (d=128) or 64 (d=64) keys, double
-// buffered one tile ahead with one barrier per tile: at d = 64, 96 and 128
-// both, and at d = 256 K, by buffer loads that write LDS directly (LDS DMA),
+// buffered one tile ahead with one barrier per tile: at d = 64, 96, 128 and
+// 256 both, by buffer loads that write LDS directly (LDS DMA),
 // each tile through a buffer resource based at its first row; the rest
 // HBM -> registers -> LDS. Global loads are buffer loads: rows past N come
 // back as zeros, with no branches. Both contractions run on
@@ -89,14 +89,17 @@ constexpr bool kMfmaPriority = D >= 64 && QB == 1;
 // the loads into registers, not their latency, were the cost. Measured
 // interleaved against the register path: K and V by DMA +2.2% at d = 128,
 // +3.8% on the long causal workload, +7.5% at d = 96 (its kernel drops to
-// 127 VGPRs, four waves per SIMD); at d = 256 K alone (+3.1%; V too -2.9%);
-// at d = 64, with four waves per SIMD forced (kMinBlocks), +0.8% to +3.3%
-// on four shapes (without the fourth wave -1.4% to +0.8%); at d = 32 DMA
-// loses (-1%).
+// 127 VGPRs, four waves per SIMD); at d = 64, with four waves per SIMD
+// forced (kMinBlocks), +0.8% to +3.3% on four shapes (without the fourth
+// wave -1.4% to +0.8%); at d = 32 DMA loses (-1%). At d = 256, with V's
+// staging registers gone the kernel fits in 247 VGPRs, two waves per SIMD
+// instead of one (404 registers with V through registers): +59% on
+// B=16 H=16 N=4096 and +54% on the long causal shape (interleaved A/B,
+// bit-identical outputs).
 template <int D>
 constexpr bool kKDma = D == 64 || D == 96 || D == 128 || D == 256;
 template <int D>
-constexpr bool kVDma = D == 64 || D == 96 || D == 128;
+constexpr bool kVDma = D == 64 || D == 96 || D == 128 || D == 256;
 // DMA tiles are addressed through a resource based at the tile's first row
 // rather than by adding the row offset to every lane's offset (two vector
 // adds per DMA instruction, ten per tile and wave at d = 128). Measured
@@ -105,12 +108,14 @@ constexpr bool kVDma = D == 64 || D == 96 || D == 128;
 // d = 256, and with the bit-select mask below +1.4% on causal d = 64.
 
 // Workgroup shapes: QB 32-query blocks per wave, NW waves per workgroup.
-// d = 96 has two, chosen at launch by the size of the grid: eight waves of
-// one block (256 rows; two workgroups per CU, four waves per SIMD) on big
-// grids, which halves the HBM -> LDS staging per FLOP (+2.7% on B=16 H=16
-// N=4096, +3.4% on the long causal shape, interleaved), else four waves. At
-// d = 64 eight waves gained +0.5% on big grids and lost 2.6-2.8% on the two
-// small workloads, so d = 64 keeps four. d = 128 has three:
+// d = 96 and 256 have two, chosen at launch by the size of the grid: eight
+// waves of one block (256 rows) on big grids, which halves the HBM -> LDS
+// staging per FLOP, else four waves. At d = 96 (two workgroups per CU, four
+// waves per SIMD) that gave +2.7% on B=16 H=16 N=4096 and +3.4% on the long
+// causal shape, at d = 256 (one per CU, two waves per SIMD) +3.9% and +6.7%
+// (interleaved A/Bs). At d = 64 eight waves gained +0.5% on big grids and
+// lost 2.6-2.8% on the two small workloads, so d = 64 keeps four. d = 128
+// has three:
 // - QB = 2, NW = 8 (512 rows a workgroup, one per CU, two waves per SIMD);
 // - QB = 2, NW = 4 (256 rows, two per CU, two waves per SIMD);
 // - QB = 1, NW = 4 (128 rows, three per CU, three waves per SIMD).
@@ -127,7 +132,7 @@ constexpr bool kVDma = D == 64 || D == 96 || D == 128;
 // Workgroups per CU the register allocation must allow.
 template <int D, int QB, int NW>
 constexpr int kMinBlocks =
-    QB == 2 ? 8 / NW : (D == 256 ? 1 : D == 64 ? 4 : D >= 96 ? 3 : 2) * kWaves / NW;
+    QB == 2 ? 8 / NW : (D == 64 ? 4 : D == 96 || D == 128 ? 3 : 2) * kWaves / NW;
 // The most query rows a workgroup has (the 32-bit offset check on Nq allows
 // for one workgroup's rows past the end).
 constexpr int kBlockMMax = 32 * 8 * 2;
@@ -542,10 +547,12 @@ void pick_shape_128(int64_t BH, int Nq, int* qb, int* nw) {
   }
 }
 
-// d = 96: eight-wave workgroups (256 rows) when the grid gives two full
-// rounds of two per CU, else four waves.
-int pick_waves_96(int64_t BH, int Nq) {
-  return BH * (((int64_t)Nq + 255) / 256) >= 4 * kCUs ? 8 : 4;
+// d = 96 and 256 (one block a wave): eight-wave workgroups (256 rows) when
+// the grid gives two full rounds of them (two per CU at d = 96, one at
+// d = 256), else four waves.
+int pick_waves_one_block(int64_t BH, int Nq, int d) {
+  const int64_t per_round = (d == 96 ? 2 : 1) * kCUs;
+  return BH * (((int64_t)Nq + 255) / 256) >= 2 * per_round ? 8 : 4;
 }
 
 // Sizes shared by every entry point; Nk only bounds the key tensors.
@@ -565,7 +572,7 @@ int check_sizes(int B, int H, int Nq, int Nk, int d, Shape* sh) {
   }
   sh->qb = 1, sh->nw = kWaves;
   if (d == 128) pick_shape_128((int64_t)B * H, Nq, &sh->qb, &sh->nw);
-  if (d == 96) sh->nw = pick_waves_96((int64_t)B * H, Nq);
+  if (d == 96 || d == 256) sh->nw = pick_waves_one_block((int64_t)B * H, Nq, d);
   sh->block = 64 * sh->nw;
   sh->block_m = 32 * sh->nw * sh->qb;
   const int64_t nq = ((int64_t)Nq + sh->block_m - 1) / sh->block_m;
@@ -607,7 +614,7 @@ hipError_t launch(const Shape& sh, const Args& a) {
 
 template <typename E, int D, bool CAUSAL>
 hipError_t launch_shape(const Shape& sh, const Args& a) {
-  if constexpr (D == 96) {
+  if constexpr (D == 96 || D == 256) {
     if (sh.nw == 8) return launch<E, D, CAUSAL, 1, 8>(sh, a);
   }
   if constexpr (D == 128) {
