@@ -328,12 +328,13 @@ def test_launch_shape_d128_follows_the_grid(lib, B, H, N, rows):
                                         (4, 16, 4000, 256), (2, 16, 4000, 128),
                                         (4, 16, 1024, 128)])
 def test_launch_shape_d96_follows_the_grid(lib, B, H, N, rows):
-    # d = 96 takes eight-wave, 256-row workgroups when the grid gives two full
-    # rounds of two per CU, else four-wave, 128-row ones
-    s = mi.attn_fwd_launch_shape(B, H, N, 96, True)
-    assert s["block_m"] == rows
-    assert s["block"] == (512 if rows == 256 else 256)
-    assert s["grid"] == B * H * ((N + rows - 1) // rows)
+    # d = 96 (and d = 32) take eight-wave, 256-row workgroups when the grid
+    # gives two full rounds of two per CU, else four-wave, 128-row ones
+    for d in (96, 32):
+        s = mi.attn_fwd_launch_shape(B, H, N, d, True)
+        assert s["block_m"] == rows
+        assert s["block"] == (512 if rows == 256 else 256)
+        assert s["grid"] == B * H * ((N + rows - 1) // rows)
 
 
 @pytest.mark.parametrize("B,H,N,rows", [(16, 16, 4096, 256), (1, 32, 16384, 256),

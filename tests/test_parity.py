@@ -481,7 +481,7 @@ def test_ex_long_sampled(d, N, causal, dt):
 # grids of two full rounds, else four. Each case below lands on one shape,
 # with ragged lengths and (causal) Nq != Nk, checked on sampled rows of a few
 # heads. d = 256 takes eight one-block waves on grids of two full rounds
-# of one workgroup per CU.
+# of one workgroup per CU, d = 32 as d = 96.
 SHAPES = [
     # (d, B, H, Nq, Nk, causal, rows per workgroup, element type)
     (128, 8, 16, 4000, 4000, False, 512, "bf16"),
@@ -500,6 +500,9 @@ SHAPES = [
     (256, 2, 16, 4000, 4000, False, 256, "bf16"),
     (256, 3, 16, 3000, 4100, True, 256, "f16"),
     (256, 1, 16, 4000, 4000, True, 128, "bf16"),
+    (32, 4, 16, 4000, 4000, True, 256, "bf16"),
+    (32, 6, 16, 3000, 4100, False, 256, "f16"),
+    (32, 2, 16, 4000, 4000, False, 128, "bf16"),
 ]
 
 

@@ -108,12 +108,13 @@ constexpr bool kVDma = D == 64 || D == 96 || D == 128 || D == 256;
 // d = 256, and with the bit-select mask below +1.4% on causal d = 64.
 
 // Workgroup shapes: QB 32-query blocks per wave, NW waves per workgroup.
-// d = 96 and 256 have two, chosen at launch by the size of the grid: eight
-// waves of one block (256 rows) on big grids, which halves the HBM -> LDS
-// staging per FLOP, else four waves. At d = 96 (two workgroups per CU, four
-// waves per SIMD) that gave +2.7% on B=16 H=16 N=4096 and +3.4% on the long
-// causal shape, at d = 256 (one per CU, two waves per SIMD) +3.9% and +6.7%
-// (interleaved A/Bs). At d = 64 eight waves gained +0.5% on big grids and
+// d = 32, 96 and 256 have two, chosen at launch by the size of the grid:
+// eight waves of one block (256 rows) on big grids, which halves the
+// HBM -> LDS staging per FLOP, else four waves. At d = 96 (two workgroups
+// per CU, four waves per SIMD) that gave +2.7% on B=16 H=16 N=4096 and +3.4%
+// on the long causal shape, at d = 256 (one per CU, two waves per SIMD)
+// +3.9% and +6.7%, at d = 32 (two per CU) +3.5% and +2.3% (interleaved
+// A/Bs). At d = 64 eight waves gained +0.5% on big grids and
 // lost 2.6-2.8% on the two small workloads, so d = 64 keeps four. d = 128
 // has three:
 // - QB = 2, NW = 8 (512 rows a workgroup, one per CU, two waves per SIMD);
@@ -547,11 +548,11 @@ void pick_shape_128(int64_t BH, int Nq, int* qb, int* nw) {
   }
 }
 
-// d = 96 and 256 (one block a wave): eight-wave workgroups (256 rows) when
-// the grid gives two full rounds of them (two per CU at d = 96, one at
-// d = 256), else four waves.
+// d = 32, 96 and 256 (one block a wave): eight-wave workgroups (256 rows)
+// when the grid gives two full rounds of them (two per CU at d = 32 and 96,
+// one at d = 256), else four waves.
 int pick_waves_one_block(int64_t BH, int Nq, int d) {
-  const int64_t per_round = (d == 96 ? 2 : 1) * kCUs;
+  const int64_t per_round = (d == 256 ? 1 : 2) * kCUs;
   return BH * (((int64_t)Nq + 255) / 256) >= 2 * per_round ? 8 : 4;
 }
 
@@ -572,7 +573,7 @@ int check_sizes(int B, int H, int Nq, int Nk, int d, Shape* sh) {
   }
   sh->qb = 1, sh->nw = kWaves;
   if (d == 128) pick_shape_128((int64_t)B * H, Nq, &sh->qb, &sh->nw);
-  if (d == 96 || d == 256) sh->nw = pick_waves_one_block((int64_t)B * H, Nq, d);
+  if (d == 32 || d == 96 || d == 256) sh->nw = pick_waves_one_block((int64_t)B * H, Nq, d);
   sh->block = 64 * sh->nw;
   sh->block_m = 32 * sh->nw * sh->qb;
   const int64_t nq = ((int64_t)Nq + sh->block_m - 1) / sh->block_m;
@@ -614,7 +615,7 @@ hipError_t launch(const Shape& sh, const Args& a) {
 
 template <typename E, int D, bool CAUSAL>
 hipError_t launch_shape(const Shape& sh, const Args& a) {
-  if constexpr (D == 96 || D == 256) {
+  if constexpr (D == 32 || D == 96 || D == 256) {
     if (sh.nw == 8) return launch<E, D, CAUSAL, 1, 8>(sh, a);
   }
   if constexpr (D == 128) {
