@@ -15,11 +15,11 @@
 //
 // Kernels on the caller's stream, no atomics, every output written once:
 //
-//  * dQ kernel: one workgroup per 128 query rows of one head (a query per
+//  * dQ kernel: one workgroup per 128 (or 256) query rows of one head (a query per
 //    lane, as in the forward), keys streamed through LDS in tiles. It also
 //    forms D_i from its own rows of O and dO and writes it to `delta`.
 //      S^T = K Q^T,  dP^T = V dO^T,  dS^T = P^T * (dP^T - D),  dQ^T += K^T dS^T
-//  * key-side kernel: one workgroup per 128 keys (a key per lane), query
+//  * key-side kernel: one workgroup per 128 (or 256) keys (a key per lane), query
 //    tiles streamed through LDS in two row-major copies (row reads and
 //    transposing reads); one pass accumulates both gradients.
 //      S = Q K^T,  dP = dO V^T,  dS = P * (dP - D),
@@ -49,7 +49,18 @@ namespace {
 
 using namespace mi_attn;
 
-constexpr int kBlockRows = 32 * kWaves;  // query rows (dQ) or keys (dK/dV) per workgroup
+// Query rows (dQ) or keys (dK/dV) per workgroup: 32 a wave, four waves a
+// workgroup and two workgroups a CU, or at d = 128 without the causal mask,
+// on big grids with long rows, eight waves, one workgroup a CU. Eight waves
+// halve the HBM -> LDS staging per FLOP (each streamed tile serves twice the
+// rows): +2.9% on B=16 H=16 N=4096 d=128 and +0.7% on B=4 H=16 N=2048, but
+// -0.8% on B=8 H=16 N=1024, where the loop is too short to hide the start
+// and end of a workgroup that has its CU to itself (measured interleaved,
+// bit-identical outputs). Causal, the bigger workgroups lose (-0.5% on
+// B=1 H=32 N=16384 d=128, -6.6% on B=8 H=16 N=2048 d=64; the last row
+// blocks of a causal grid carry the most work), and so they do at d = 32
+// (-3.8%) and 96 (-2.0%).
+constexpr int kBlockRows = 32 * kWaves;  // with four waves; the size checks use it
 
 // Rows per streamed tile (keys in the dQ kernel, queries in the dK/dV
 // kernel).
@@ -77,13 +88,13 @@ constexpr int kLayoutD = D == 96 ? 128 : D;
 // keeps its DMA offsets, two row-read bases (the chunk pair's low bits XOR
 // the swizzle take two values) and two transposing-read offsets (rows +0
 // and +8 of a slice).
-template <int D, int BR>
+template <int D, int BR, int WAVES>
 struct SwzTile {
   static constexpr int DL = kLayoutD<D>;
   static constexpr int P = DL % 64 == 32 ? DL : DL + 32;  // row pitch, elements
   static constexpr int SLOTS = P / 8, CPR = DL / 8;
   static constexpr int NINSTR = (BR * SLOTS + 63) / 64;
-  static constexpr int NW = (NINSTR + kWaves - 1) / kWaves;  // per wave, at most
+  static constexpr int NW = (NINSTR + WAVES - 1) / WAVES;  // per wave, at most
   static constexpr int SPAN = NINSTR * 1024;
   static constexpr uint32_t kNoFetch = 0x80000000u;  // + row0 * D * 2 < 2^31
   static_assert((P * 2) % 128 == 64, "pitch: an odd multiple of 64 bytes");
@@ -93,7 +104,7 @@ struct SwzTile {
   __device__ __forceinline__ SwzTile(int wave, int lane) {
 #pragma unroll
     for (int i = 0; i < NW; ++i) {
-      const int slot = 64 * (wave + kWaves * i) + lane;
+      const int slot = 64 * (wave + WAVES * i) + lane;
       const int row = slot / SLOTS, pc = slot % SLOTS;
       const int c = pc ^ swz(row);  // logical chunk held by physical chunk pc
       off[i] = row < BR && pc < CPR && c < D / 8 ? (uint32_t)(row * D + 8 * c) * 2 : kNoFetch;
@@ -110,7 +121,7 @@ struct SwzTile {
   __device__ __forceinline__ void issue(rsrc_t r, lds_char* tile, int wave, int row0) const {
 #pragma unroll
     for (int i = 0; i < NW; ++i) {
-      const int u = wave + kWaves * i;
+      const int u = wave + WAVES * i;
       if (u < NINSTR) load16_lds(r, tile + 1024 * u, off[i] + (uint32_t)row0 * D * 2);
     }
   }
@@ -143,14 +154,14 @@ __device__ __forceinline__ float lse_log2(float lse, bool valid) {
 
 // ------------------------------------------------------------- dQ kernel --
 
-template <typename E, int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(
+template <typename E, int D, bool CAUSAL, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void attn_bwd_dq_kernel(
     const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict__ V,
     const E* __restrict__ O, const float* __restrict__ LSE, const E* __restrict__ dO,
     E* __restrict__ dQ, float* __restrict__ Delta, int BH, int Nq, int Nk, int nq, float c,
     float dq_scale) {
   constexpr int BN = kTileRows<D>;
-  using G = SwzTile<D, BN>;
+  using G = SwzTile<D, BN, NW>;
   constexpr int NKB = BN / 32;
   // Stage: K | V (K is read both as rows and as columns).
   constexpr int V_OFF = G::SPAN;
@@ -164,7 +175,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(
   const int lane = tid & 63, col = lane & 31, half = lane >> 5;
   int bh, qt;
   map_block(blockIdx.x, BH, nq, CAUSAL, bh, qt);
-  const int q0 = qt * kBlockRows;
+  const int q0 = qt * 32 * NW;
   const int qw = q0 + 32 * wave;
   const int qi = qw + col;
   const int off = Nk - Nq;  // query i sits at key position i + off
@@ -203,7 +214,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(delta), rd, qi * 4, 0, 0);
   }
 
-  const int kv_end = CAUSAL ? min(Nk, q0 + kBlockRows + off) : Nk;
+  const int kv_end = CAUSAL ? min(Nk, q0 + 32 * NW + off) : Nk;
   const int nt = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
   const int wave_kv_end = CAUSAL ? min(Nk, qw + 32 + off) : Nk;
 
@@ -312,10 +323,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(
 
 // LDS stage of the key-side kernel:
 //   Q (rows: S = Q K^T; columns: dK) | dO (rows: dP; columns: dV) | lse | D
-template <int D>
+template <int D, int NW>
 struct KeyStage {
   static constexpr int BQ = kTileRows<D>;
-  using G = SwzTile<D, BQ>;
+  using G = SwzTile<D, BQ, NW>;
   static constexpr int DO_OFF = G::SPAN;
   static constexpr int L_OFF = 2 * G::SPAN;
   static constexpr int D_OFF = L_OFF + BQ * 4;
@@ -323,13 +334,13 @@ struct KeyStage {
   static_assert(BYTES % 16 == 0 && L_OFF % 16 == 0, "16-byte aligned LDS tiles");
 };
 
-template <typename E, int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 2) void attn_bwd_kv_kernel(
+template <typename E, int D, bool CAUSAL, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void attn_bwd_kv_kernel(
     const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict__ V,
     const float* __restrict__ LSE, const E* __restrict__ dO, const float* __restrict__ Delta,
     E* __restrict__ dK, E* __restrict__ dV, int BH, int Nq, int Nk, int nk, float c,
     float dk_scale) {
-  using S_ = KeyStage<D>;
+  using S_ = KeyStage<D, NW>;
   using G = typename S_::G;
   constexpr int BQ = S_::BQ;
   constexpr int NQB = BQ / 32;
@@ -346,7 +357,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_kv_kernel(
   // Causal: key tile 0 sees the most queries; map_block deals the last index
   // first, so number the key tiles from the end.
   if (CAUSAL) kt = nk - 1 - kt;
-  const int k0 = kt * kBlockRows;
+  const int k0 = kt * 32 * NW;
   const int kw = k0 + 32 * wave;  // first key of this wave
   const int kj = kw + col;        // this lane's key
   const int off = Nk - Nq;        // query i sees key j iff j <= i + off (causal)
@@ -518,12 +529,26 @@ struct BwdArgs {
   const float* lse;
   void *dq, *dk, *dv;
   float* delta;
-  int BH, Nq, Nk, nq, nk;
+  int BH, Nq, Nk, nq, nk, nw;
   float c, scale;
   hipStream_t stream;
 };
 
-template <typename E, int D, bool CAUSAL>
+constexpr int64_t kCUs = 256;  // gfx950 parts have 256 CUs
+
+// Waves per workgroup (both kernels): eight at d = 128 without the causal
+// mask when both axes have at least 2048 rows, both grids give two rounds of
+// one eight-wave workgroup per CU and the offsets of one such workgroup past
+// the end stay within 32 bits, else four.
+int pick_waves(int64_t BH, int Nq, int Nk, int d, bool causal) {
+  if (d != 128 || causal || Nq < 2048 || Nk < 2048) return 4;
+  auto grid = [&](int n) { return BH * (((int64_t)n + 255) / 256); };
+  if (grid(Nq) < 2 * kCUs || grid(Nk) < 2 * kCUs) return 4;
+  if ((int64_t)(Nq > Nk ? Nq : Nk) * d * 2 + (int64_t)256 * d * 2 > INT32_MAX) return 4;
+  return 8;
+}
+
+template <typename E, int D, bool CAUSAL, int NW>
 hipError_t launch_bwd(const BwdArgs& a) {
   const E* q = static_cast<const E*>(a.q);
   const E* k = static_cast<const E*>(a.k);
@@ -541,16 +566,16 @@ hipError_t launch_bwd(const BwdArgs& a) {
   if (nq > 0) {
     void* args[] = {&q, &k, &v, &o, &lse, &d_o, &dq, &delta, &BH, &Nq, &Nk, &nq, &c, &scale};
     const hipError_t err =
-        hipLaunchKernel(reinterpret_cast<const void*>(&attn_bwd_dq_kernel<E, D, CAUSAL>),
-                        dim3(BH * nq), dim3(kThreads), args, 0, a.stream);
+        hipLaunchKernel(reinterpret_cast<const void*>(&attn_bwd_dq_kernel<E, D, CAUSAL, NW>),
+                        dim3(BH * nq), dim3(64 * NW), args, 0, a.stream);
     if (err != hipSuccess) return err;
   }
   if (nk > 0) {
     void* args[] = {&q, &k, &v, &lse, &d_o, &delta, &dk, &dv, &BH, &Nq, &Nk, &nk, &c, &scale};
     auto go = [&](const void* fn) {
-      return hipLaunchKernel(fn, dim3(BH * nk), dim3(kThreads), args, 0, a.stream);
+      return hipLaunchKernel(fn, dim3(BH * nk), dim3(64 * NW), args, 0, a.stream);
     };
-    return go(reinterpret_cast<const void*>(&attn_bwd_kv_kernel<E, D, CAUSAL>));
+    return go(reinterpret_cast<const void*>(&attn_bwd_kv_kernel<E, D, CAUSAL, NW>));
   }
   return hipSuccess;
 }
@@ -558,10 +583,12 @@ hipError_t launch_bwd(const BwdArgs& a) {
 template <typename E>
 hipError_t launch_bwd_type(const BwdArgs& a, int d, bool causal) {
   switch (d) {
-    case 32: return causal ? launch_bwd<E, 32, true>(a) : launch_bwd<E, 32, false>(a);
-    case 64: return causal ? launch_bwd<E, 64, true>(a) : launch_bwd<E, 64, false>(a);
-    case 96: return causal ? launch_bwd<E, 96, true>(a) : launch_bwd<E, 96, false>(a);
-    default: return causal ? launch_bwd<E, 128, true>(a) : launch_bwd<E, 128, false>(a);
+    case 32: return causal ? launch_bwd<E, 32, true, 4>(a) : launch_bwd<E, 32, false, 4>(a);
+    case 64: return causal ? launch_bwd<E, 64, true, 4>(a) : launch_bwd<E, 64, false, 4>(a);
+    case 96: return causal ? launch_bwd<E, 96, true, 4>(a) : launch_bwd<E, 96, false, 4>(a);
+    default:
+      if (causal) return launch_bwd<E, 128, true, 4>(a);
+      return a.nw == 8 ? launch_bwd<E, 128, false, 8>(a) : launch_bwd<E, 128, false, 4>(a);
   }
 }
 
@@ -576,8 +603,10 @@ extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void*
   if ((int64_t)Nq * d * 2 + (int64_t)kBlockRows * d * 2 > INT32_MAX) return ATTN_ERR_SHAPE;
   if ((int64_t)Nk * d * 2 + (int64_t)kBlockRows * d * 2 > INT32_MAX) return ATTN_ERR_SHAPE;
   const int64_t BH = (int64_t)B * H;
-  const int64_t nq = ((int64_t)Nq + kBlockRows - 1) / kBlockRows;
-  const int64_t nk = ((int64_t)Nk + kBlockRows - 1) / kBlockRows;
+  const int nw = pick_waves(BH, Nq, Nk, d, causal != 0);
+  const int64_t rows = 32 * nw;
+  const int64_t nq = ((int64_t)Nq + rows - 1) / rows;
+  const int64_t nk = ((int64_t)Nk + rows - 1) / rows;
   if (BH * nq > INT32_MAX || BH * nk > INT32_MAX) return ATTN_ERR_SHAPE;
   if (dtype != ATTN_BF16 && dtype != ATTN_F16) return ATTN_ERR_DTYPE;
   uint32_t sbits;
@@ -605,7 +634,7 @@ extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void*
   }
 
   const BwdArgs a{q, k, v, o, d_o, lse, dq, dk, dv, delta, (int)BH, Nq, Nk, (int)nq, (int)nk,
-                  scale * kLog2e, scale, static_cast<hipStream_t>(stream)};
+                  nw, scale * kLog2e, scale, static_cast<hipStream_t>(stream)};
   const hipError_t err = dtype == ATTN_BF16 ? launch_bwd_type<__bf16>(a, d, causal != 0)
                                             : launch_bwd_type<_Float16>(a, d, causal != 0);
   return err == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
