@@ -58,7 +58,8 @@ using namespace mi_attn;
 // and end of a workgroup that has its CU to itself (measured interleaved,
 // bit-identical outputs). Causal, the bigger workgroups lose (-0.5% on
 // B=1 H=32 N=16384 d=128, -6.6% on B=8 H=16 N=2048 d=64; the last row
-// blocks of a causal grid carry the most work), and so they do at d = 32
+// blocks of a causal grid carry the most work; in the dK/dV kernel alone
+// -2.2% on the first and -3.8% on B=4 H=16 N=2048), and so they do at d = 32
 // (-3.8%), 64 (-2.8% on B=16 H=16 N=4096, -3.2% on B=8 H=16 N=2048) and 96
 // (-2.0%).
 constexpr int kBlockRows = 32 * kWaves;  // with four waves; the size checks use it
