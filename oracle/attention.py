@@ -123,13 +123,18 @@ def attention_ref(q, k, v, scale, causal):
     return o, lse
 
 
-def attend_head_grad(q, k, v, do, scale, causal, q_pos=None):
+def attend_head_grad(q, k, v, do, scale, causal, q_pos=None, chunk=1024):
     """Gradients of one head: returns (dq [M,d], dk [N,d], dv [N,d]) in float64,
     of L = sum(do * o) with o the output of attend_head(q, k, v, scale, causal).
 
     The weights are recomputed from the definition exactly as attend_head
-    forms them (full score matrix, masked entries -inf, max subtracted); then
+    forms them (full score rows, masked entries -inf, max subtracted); then
     the chain rule of the module docstring. q_pos as for attend_head.
+
+    L is a sum over query rows, and a row's weights depend on that row alone,
+    so the rows are taken ``chunk`` at a time only to bound memory: each chunk
+    gives its rows' dq outright and adds its rows' share of dk and dv (the
+    sums over i in dV = P^T dO and dK = scale dS^T Q, split by rows).
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -144,26 +149,32 @@ def attend_head_grad(q, k, v, do, scale, causal, q_pos=None):
         q_pos = np.arange(m_rows) + (n_keys - m_rows)
     q_pos = np.asarray(q_pos, dtype=np.int64)
 
-    # softmax weights P [M, N]
-    s = scale * (q @ k.T)
-    if causal:
-        s[np.arange(n_keys)[None, :] > q_pos[:, None]] = -np.inf
-    if n_keys:
-        m = s.max(axis=1, keepdims=True)
-    else:
-        m = np.full((m_rows, 1), -np.inf)
-    empty = np.isneginf(m[:, 0])
-    m[empty] = 0.0
-    w = np.exp(s - m)
-    l = w.sum(axis=1, keepdims=True)
-    l[empty] = 1.0
-    p = w / l  # rows that see no key: all zero
+    dq = np.empty((m_rows, d), dtype=np.float64)
+    dk = np.zeros((n_keys, d), dtype=np.float64)
+    dv = np.zeros((n_keys, v.shape[1]), dtype=np.float64)
+    key_idx = np.arange(n_keys)
+    for r0 in range(0, m_rows, chunk):
+        r1 = min(r0 + chunk, m_rows)
+        # softmax weights P of these rows over the full key axis
+        s = scale * (q[r0:r1] @ k.T)
+        if causal:
+            s[key_idx[None, :] > q_pos[r0:r1, None]] = -np.inf
+        if n_keys:
+            m = s.max(axis=1, keepdims=True)
+        else:
+            m = np.full((r1 - r0, 1), -np.inf)
+        empty = np.isneginf(m[:, 0])
+        m[empty] = 0.0
+        w = np.exp(s - m)
+        l = w.sum(axis=1, keepdims=True)
+        l[empty] = 1.0
+        p = w / l  # rows that see no key: all zero
 
-    dv = p.T @ do
-    dp = do @ v.T
-    ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
-    dq = scale * (ds @ k)
-    dk = scale * (ds.T @ q)
+        dv += p.T @ do[r0:r1]
+        dp = do[r0:r1] @ v.T
+        ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+        dq[r0:r1] = scale * (ds @ k)
+        dk += scale * (ds.T @ q[r0:r1])
     return dq, dk, dv
 
 

@@ -7,6 +7,7 @@ definition (softmax rows are shift-invariant and sum to one). Each planted
 mistake below must fail at least one pin.
 """
 
+import functools
 import math
 import os
 import re
@@ -260,6 +261,64 @@ PINS = [pin_golden, pin_finite_differences, pin_torch_autograd, pin_key_shift_in
 @pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
 def test_oracle_grad_meets_pin(pin):
     assert pin(attend_head_grad)
+
+
+@pytest.mark.parametrize("chunk", [1, 2, 3])
+def test_chunked_oracle_grad_meets_every_pin(chunk):
+    """The pins again with the query rows taken a few at a time, so that every
+    pin shape (up to 9 rows) spans several chunks and a ragged last one: a
+    chunk that drops its share of dk or dv, or writes dq rows in the wrong
+    place, fails them."""
+    grad = functools.partial(attend_head_grad, chunk=chunk)
+    failed = [p.__name__ for p in PINS if not p(grad)]
+    assert not failed, failed
+
+
+def _dropped_chunk_share(q, k, v, do, scale, causal, q_pos=None):
+    """A chunked gradient with one slip: dk and dv keep only the last chunk's
+    share (assigned instead of added)."""
+    q, k, v, do = (np.asarray(t, np.float64) for t in (q, k, v, do))
+    m, n = q.shape[0], k.shape[0]
+    pos = np.arange(m) + (n - m) if q_pos is None else np.asarray(q_pos)
+    dq = np.empty_like(q)
+    dk = dv = None
+    for r0 in range(0, m, 2):
+        rows = np.arange(r0, min(r0 + 2, m))
+        dq[rows], dk, dv = attend_head_grad(q[rows], k, v, do[rows], scale, causal,
+                                            q_pos=pos[rows])
+    return dq, dk, dv
+
+
+def test_dropped_chunk_share_fails_a_pin():
+    assert [p.__name__ for p in PINS if not p(_dropped_chunk_share)]
+
+
+@pytest.mark.parametrize("m,n", [(25, 25), (25, 40), (40, 25), (1, 30)])
+def test_chunk_size_does_not_change_gradients(m, n):
+    q, k, v, do = _rand((m, 6), 100), _rand((n, 6), 101), _rand((n, 6), 102), _rand((m, 6), 103)
+    for causal in (False, True):
+        ref = attend_head_grad(q, k, v, do, 0.45, causal)
+        for chunk in (1, 4, 7, m):
+            got = attend_head_grad(q, k, v, do, 0.45, causal, chunk=chunk)
+            for g, r in zip(got, ref):
+                assert g.shape == r.shape and np.allclose(g, r, rtol=0, atol=1e-13)
+
+
+def test_row_sample_gradients_sum_to_the_full_key_side():
+    """Because L sums over rows, dk and dv of a row subset (with its
+    positions) summed over a partition of the rows equal the full result; this
+    is how full-size parity builds the key-side gradients of long heads."""
+    m = n = 37
+    q, k, v, do = _rand((m, 5), 110), _rand((n, 5), 111), _rand((n, 5), 112), _rand((m, 5), 113)
+    for causal in (False, True):
+        dq, dk, dv = attend_head_grad(q, k, v, do, 0.6, causal)
+        sk, sv = np.zeros_like(dk), np.zeros_like(dv)
+        for rows in (np.arange(0, 10), np.arange(10, 31), np.arange(31, 37)):
+            rq, rk, rv = attend_head_grad(q[rows], k, v, do[rows], 0.6, causal, q_pos=rows)
+            assert np.allclose(rq, dq[rows], atol=1e-13)
+            sk += rk
+            sv += rv
+        assert np.allclose(sk, dk, atol=1e-13) and np.allclose(sv, dv, atol=1e-13)
 
 
 # ------------------------------------------------------------ planted mistakes --
