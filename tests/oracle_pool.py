@@ -7,11 +7,11 @@ import numpy as np
 from oracle import attend_head
 
 
-def limit_blas_threads():
-    """Pool initializer: one BLAS thread per worker process."""
+def limit_blas_threads(threads=1):
+    """Pool initializer: `threads` BLAS threads per worker process."""
     try:
         from threadpoolctl import threadpool_limits
-        threadpool_limits(1)
+        threadpool_limits(threads)
     except ImportError:
         pass
 
