@@ -16,8 +16,9 @@
  * where every key is visible when causal == 0, and key j is visible to query i
  * iff j <= i when causal != 0. Masked keys carry weight exactly zero.
  *
- * All calls are thread-safe, keep no state between calls, allocate nothing,
- * never print and never abort.
+ * All calls are thread-safe, allocate nothing, never print and never abort.
+ * None keeps state between calls, except that attn_bwd_noalloc keeps its
+ * static device buffer (and the address it looked up) for the process.
  */
 #ifndef MI_ATTN_H
 #define MI_ATTN_H
@@ -36,7 +37,8 @@ typedef enum {
   ATTN_ERR_ALIAS = -6,     /* o or lse overlaps an input, or o overlaps lse */
   ATTN_ERR_SCALE = -7,     /* scale is NaN or infinite */
   ATTN_ERR_LAUNCH = -8,    /* the HIP launch failed (no gfx950 device, bad stream, ...) */
-  ATTN_ERR_DTYPE = -9      /* dtype is not an attn_dtype value */
+  ATTN_ERR_DTYPE = -9,     /* dtype is not an attn_dtype value */
+  ATTN_ERR_SCRATCH = -10   /* attn_bwd_noalloc: B*H*Nq exceeds its static buffer */
 } attn_status;
 
 /* Element type of q, k, v and o (attn_fwd_ex). lse is always float32. */
@@ -155,6 +157,31 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
              const void* d_o, void* dq, void* dk, void* dv, float* delta, int B, int H,
              int Nq, int Nk, int d, int dtype, float scale, int causal, void* stream);
+
+/*
+ * attn_bwd_noalloc - attn_bwd without the `delta` workspace, for callers that
+ * cannot allocate device memory (code under stream capture, tight serving
+ * loops, harnesses that forbid allocation).
+ *
+ * Arguments, results and errors are those of attn_bwd with `delta` left out:
+ * the row sums D_i go to a static device buffer of the library instead, room
+ * for B*H*Nq <= 4194304 rows (16 MiB, reserved on each device the library
+ * runs on until the process ends). Larger problems return ATTN_ERR_SCRATCH
+ * before any HIP call. The call allocates nothing: on its first call on a
+ * device (the current one) it looks up that device's address of the buffer;
+ * if the runtime cannot give it the call returns ATTN_ERR_LAUNCH.
+ *
+ * Every call on one device shares that device's buffer. Calls that may run
+ * at the same time on one device (different streams, or different host
+ * threads without ordering) race on it and give undefined gradients;
+ * serialise them, e.g. on one stream. The buffer needs no clearing: each call
+ * writes the rows it reads before reading them, in stream order. Results are
+ * bit-identical to attn_bwd's.
+ */
+int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                     const float* lse, const void* d_o, void* dq, void* dk, void* dv, int B,
+                     int H, int Nq, int Nk, int d, int dtype, float scale, int causal,
+                     void* stream);
 
 /* attn_strerror - static, NUL-terminated description of a status code
  * (an unknown code yields "unknown status"). Never NULL. */

@@ -18,7 +18,7 @@ HEADER = os.path.join(ROOT, "include", "mi_attn.h")
 
 OK, ERR_NULL, ERR_SHAPE, ERR_HEADDIM, ERR_ALIGN, ERR_ALIAS, ERR_SCALE, ERR_LAUNCH = (
     0, -1, -2, -3, -5, -6, -7, -8)
-ERR_DTYPE = -9
+ERR_DTYPE, ERR_SCRATCH = -9, -10
 
 MIB = 1 << 20
 # Stand-in device addresses, 1 MiB apart and 256-byte aligned.
@@ -40,8 +40,8 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["attn_bwd", "attn_fwd", "attn_fwd_cross", "attn_fwd_ex",
-                                    "attn_fwd_launch_shape", "attn_strerror"]
+    assert declared_functions() == ["attn_bwd", "attn_bwd_noalloc", "attn_fwd", "attn_fwd_cross",
+                                    "attn_fwd_ex", "attn_fwd_launch_shape", "attn_strerror"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -66,11 +66,11 @@ def test_no_extra_exported_c_symbols():
 def test_strerror_covers_every_status(lib):
     seen = set()
     for code in (OK, ERR_NULL, ERR_SHAPE, ERR_HEADDIM, ERR_ALIGN, ERR_ALIAS,
-                 ERR_SCALE, ERR_LAUNCH, ERR_DTYPE):
+                 ERR_SCALE, ERR_LAUNCH, ERR_DTYPE, ERR_SCRATCH):
         msg = mi.attn_strerror(code)
         assert msg and msg != "unknown status"
         seen.add(msg)
-    assert len(seen) == 9
+    assert len(seen) == 10
     assert mi.attn_strerror(12345) == "unknown status"
 
 
@@ -292,6 +292,43 @@ def test_bwd_empty_sides(lib):
     assert bwd(lib, Nq=0, q=None, o=None, lse=None, do=None, dq=None, delta=None,
                k=None) == ERR_NULL
     assert bwd(lib, Nk=0, k=None, v=None, dk=None, dv=None, q=None) == ERR_NULL
+
+
+def bwd_noalloc(lib, d=128, dtype=0, B=2, H=3, Nq=100, Nk=70, scale=0.125, causal=0,
+                **ptrs):
+    p = dict(q=BQ_, k=BK_, v=BV_, o=BO_, lse=BL_, do=BDO_, dq=BDQ_, dk=BDK_, dv=BDV_)
+    p.update(ptrs)
+    return lib.attn_bwd_noalloc(p["q"], p["k"], p["v"], p["o"], p["lse"], p["do"], p["dq"],
+                                p["dk"], p["dv"], B, H, Nq, Nk, d, dtype, scale, causal, None)
+
+
+def test_bwd_noalloc_validates_like_attn_bwd(lib):
+    """Every argument check of attn_bwd, without the delta argument; all of
+    them come before the one-time lookup of the static buffer."""
+    for d in (0, 16, 256):
+        assert bwd_noalloc(lib, d=d) == ERR_HEADDIM
+    assert bwd_noalloc(lib, dtype=2) == ERR_DTYPE
+    assert bwd_noalloc(lib, scale=float("inf")) == ERR_SCALE
+    assert bwd_noalloc(lib, Nk=-1) == ERR_SHAPE
+    for name in ("q", "k", "v", "o", "lse", "do", "dq", "dk", "dv"):
+        assert bwd_noalloc(lib, **{name: None}) == ERR_NULL, name
+    assert bwd_noalloc(lib, dk=BDQ_) == ERR_ALIAS
+    assert bwd_noalloc(lib, dq=BO_) == ERR_ALIAS
+    assert bwd_noalloc(lib, dv=BDV_ + 4) == ERR_ALIGN
+    assert bwd_noalloc(lib, lse=BL_ + 2) == ERR_ALIGN
+    assert bwd_noalloc(lib, B=0) == OK
+    assert bwd_noalloc(lib, Nq=0, Nk=0, **{n: None for n in ("q", "k", "v", "o", "lse", "do",
+                                                             "dq", "dk", "dv")}) == OK
+
+
+@pytest.mark.parametrize("B,H,Nq", [(1, 1, 4194305), (16, 16, 16385), (64, 64, 1025)])
+def test_bwd_noalloc_rejects_more_rows_than_its_buffer(lib, B, H, Nq):
+    """B*H*Nq beyond 4194304 rows (the static buffer's 16 MiB of floats) is
+    refused before anything else is looked at; exactly the limit passes that
+    check (and then fails on a NULL pointer here)."""
+    assert bwd_noalloc(lib, B=B, H=H, Nq=Nq, d=64) == ERR_SCRATCH
+    assert bwd_noalloc(lib, B=B, H=H, Nq=Nq, d=64, q=None) == ERR_SCRATCH
+    assert bwd_noalloc(lib, B=1, H=1, Nq=4194304, d=64, q=None) == ERR_NULL
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):

@@ -13,7 +13,8 @@ import ctypes
 import math
 import os
 
-__all__ = ["attn_fwd", "attn_fwd_cross", "attn_fwd_ex", "attn_bwd", "attn_strerror",
+__all__ = ["attn_fwd", "attn_fwd_cross", "attn_fwd_ex", "attn_bwd", "attn_bwd_noalloc",
+           "attn_strerror",
            "attn_fwd_launch_shape", "lib_path", "load_library", "AttnError", "ATTN_BF16",
            "ATTN_F16"]
 
@@ -54,6 +55,8 @@ def load_library():
     lib.attn_fwd_ex.restype = i32
     lib.attn_bwd.argtypes = [vp] * 10 + [i32] * 6 + [f32, i32, vp]
     lib.attn_bwd.restype = i32
+    lib.attn_bwd_noalloc.argtypes = [vp] * 9 + [i32] * 6 + [f32, i32, vp]
+    lib.attn_bwd_noalloc.restype = i32
     lib.attn_strerror.argtypes = [i32]
     lib.attn_strerror.restype = ctypes.c_char_p
     ip = ctypes.POINTER(i32)
@@ -224,6 +227,31 @@ def _like(t, ref, shape, dtype, name):
     return t
 
 
+def _bwd_args(q, k, v, o, lse, do, scale, dq, dk, dv):
+    """Checks and outputs shared by the two backward calls."""
+    import torch
+
+    _check_inputs(q, k, v, dtypes=(torch.bfloat16, torch.float16))
+    B, H, Nq, d = q.shape
+    for name, t in (("o", o), ("do", do)):
+        if (not isinstance(t, torch.Tensor) or tuple(t.shape) != tuple(q.shape)
+                or t.dtype != q.dtype or t.device != q.device or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous tensor shaped like q, of q's dtype")
+    if (not isinstance(lse, torch.Tensor) or tuple(lse.shape) != (B, H, Nq)
+            or lse.dtype != torch.float32 or lse.device != q.device or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous float32 tensor [B, H, Nq]")
+    dq = _like(dq, q, q.shape, q.dtype, "dq")
+    dk = _like(dk, q, k.shape, q.dtype, "dk")
+    dv = _like(dv, q, k.shape, q.dtype, "dv")
+    dtype = ATTN_BF16 if q.dtype == torch.bfloat16 else ATTN_F16
+    scale = _default_scale(d) if scale is None else scale
+    return dq, dk, dv, dtype, float(scale)
+
+
+def _ptr(t):
+    return t.data_ptr() if t.numel() else 0
+
+
 def attn_bwd(q, k, v, o, lse, do, scale=None, causal=False, dq=None, dk=None, dv=None,
              delta=None, stream=None):
     """dq, dk, dv = gradients of sum(do * o) where o, lse = attn_fwd_ex(q, k, v,
@@ -238,27 +266,39 @@ def attn_bwd(q, k, v, o, lse, do, scale=None, causal=False, dq=None, dk=None, dv
     import torch
 
     lib = load_library()
-    _check_inputs(q, k, v, dtypes=(torch.bfloat16, torch.float16))
+    dq, dk, dv, dtype, scale = _bwd_args(q, k, v, o, lse, do, scale, dq, dk, dv)
     B, H, Nq, d = q.shape
     Nk = k.shape[2]
-    for name, t in (("o", o), ("do", do)):
-        if (not isinstance(t, torch.Tensor) or tuple(t.shape) != tuple(q.shape)
-                or t.dtype != q.dtype or t.device != q.device or not t.is_contiguous()):
-            raise ValueError(f"{name} must be a contiguous tensor shaped like q, of q's dtype")
-    if (not isinstance(lse, torch.Tensor) or tuple(lse.shape) != (B, H, Nq)
-            or lse.dtype != torch.float32 or lse.device != q.device or not lse.is_contiguous()):
-        raise ValueError("lse must be a contiguous float32 tensor [B, H, Nq]")
-    dq = _like(dq, q, q.shape, q.dtype, "dq")
-    dk = _like(dk, q, k.shape, q.dtype, "dk")
-    dv = _like(dv, q, k.shape, q.dtype, "dv")
     delta = _like(delta, q, (B, H, Nq), torch.float32, "delta")
-    dtype = ATTN_BF16 if q.dtype == torch.bfloat16 else ATTN_F16
-    scale = _default_scale(d) if scale is None else scale
-    ptr = lambda t: t.data_ptr() if t.numel() else 0  # noqa: E731
     with torch.cuda.device(q.device):
-        rc = lib.attn_bwd(ptr(q), ptr(k), ptr(v), ptr(o), ptr(lse), ptr(do), ptr(dq), ptr(dk),
-                          ptr(dv), ptr(delta), B, H, Nq, Nk, d, dtype, float(scale),
+        rc = lib.attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq),
+                          _ptr(dk), _ptr(dv), _ptr(delta), B, H, Nq, Nk, d, dtype, scale,
                           int(bool(causal)), _stream_handle(q, stream))
+    if rc:
+        raise AttnError(rc, attn_strerror(rc))
+    return dq, dk, dv
+
+
+def attn_bwd_noalloc(q, k, v, o, lse, do, dq, dk, dv, scale=None, causal=False, stream=None):
+    """attn_bwd into the given dq, dk, dv, with the row sums kept in the
+    library's static device buffer: this call allocates no device memory
+    (B*H*Nq up to 4194304 rows). Calls that overlap on one device race on that
+    buffer. Queued on ``stream`` (default: torch's current stream of q's
+    device); nothing synchronises.
+    """
+    import torch
+
+    lib = load_library()
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a preallocated torch.Tensor")
+    dq, dk, dv, dtype, scale = _bwd_args(q, k, v, o, lse, do, scale, dq, dk, dv)
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    with torch.cuda.device(q.device):
+        rc = lib.attn_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
+                                  _ptr(dq), _ptr(dk), _ptr(dv), B, H, Nq, Nk, d, dtype, scale,
+                                  int(bool(causal)), _stream_handle(q, stream))
     if rc:
         raise AttnError(rc, attn_strerror(rc))
     return dq, dk, dv

@@ -40,6 +40,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "common.h"
@@ -594,12 +595,45 @@ hipError_t launch_bwd_type(const BwdArgs& a, int d, bool causal) {
   }
 }
 
+// ----------------------------------------------------- static scratch --
+
+// Row sums D for attn_bwd_noalloc, in a static device array instead of a
+// caller buffer: kScratchRows floats (16 MiB) on each device the library
+// runs on, held until the process ends. Host code never uses the array's
+// name as an address (on the host it is only a stand-in); it asks the runtime
+// for the device address once per device and passes that to the kernels.
+constexpr int64_t kScratchRows = int64_t(1) << 22;  // B * H * Nq at most
+
 }  // namespace
 
-extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void* o,
-                        const float* lse, const void* d_o, void* dq, void* dk, void* dv,
-                        float* delta, int B, int H, int Nq, int Nk, int d, int dtype,
-                        float scale, int causal, void* stream) {
+static __device__ __align__(256) float scratch[kScratchRows];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_at[kMaxDevices];  // device address of `scratch`, per device
+
+// The current device's address of `scratch`, looked up on the first call on
+// that device (with it current); NULL if the runtime cannot give it.
+float* scratch_rows() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_at[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch_at[dev] = static_cast<float*>(ptr);
+  }
+  return g_scratch_at[dev];
+}
+
+// Validation and launch behind both backward entry points. With use_scratch
+// the row sums D go to the library's own buffer (`delta` is ignored), so no
+// caller buffer needs to be checked for them.
+int bwd_run(const void* q, const void* k, const void* v, const void* o, const float* lse,
+            const void* d_o, void* dq, void* dk, void* dv, float* delta, bool use_scratch, int B,
+            int H, int Nq, int Nk, int d, int dtype, float scale, int causal, void* stream) {
   if (B < 0 || H < 0 || Nq < 0 || Nk < 0) return ATTN_ERR_SHAPE;
   if (d != 32 && d != 64 && d != 96 && d != 128) return ATTN_ERR_HEADDIM;
   if ((int64_t)Nq * d * 2 + (int64_t)kBlockRows * d * 2 > INT32_MAX) return ATTN_ERR_SHAPE;
@@ -610,29 +644,34 @@ extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void*
   const int64_t nq = ((int64_t)Nq + rows - 1) / rows;
   const int64_t nk = ((int64_t)Nk + rows - 1) / rows;
   if (BH * nq > INT32_MAX || BH * nk > INT32_MAX) return ATTN_ERR_SHAPE;
+  if (use_scratch && BH * Nq > kScratchRows) return ATTN_ERR_SCRATCH;
   if (dtype != ATTN_BF16 && dtype != ATTN_F16) return ATTN_ERR_DTYPE;
   uint32_t sbits;
   memcpy(&sbits, &scale, 4);
   if ((sbits & 0x7f800000u) == 0x7f800000u) return ATTN_ERR_SCALE;
   if (BH == 0 || (Nq == 0 && Nk == 0)) return ATTN_OK;
-  if (Nq > 0 && (!q || !o || !lse || !d_o || !dq || !delta)) return ATTN_ERR_NULL;
+  if (Nq > 0 && (!q || !o || !lse || !d_o || !dq || (!use_scratch && !delta))) return ATTN_ERR_NULL;
   if (Nk > 0 && (!k || !v || !dk || !dv)) return ATTN_ERR_NULL;
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)d_o |
        (uintptr_t)dq | (uintptr_t)dk | (uintptr_t)dv) & 15)
     return ATTN_ERR_ALIGN;
-  if (((uintptr_t)lse | (uintptr_t)delta) & 3) return ATTN_ERR_ALIGN;
+  if (((uintptr_t)lse | (use_scratch ? 0 : (uintptr_t)delta)) & 3) return ATTN_ERR_ALIGN;
   const size_t qb = (size_t)BH * Nq * d * 2, kb = (size_t)BH * Nk * d * 2;
   const size_t lb = (size_t)BH * Nq * 4;
   const struct {
     const void* p;
     size_t n;
   } in[] = {{q, qb}, {k, kb}, {v, kb}, {o, qb}, {lse, lb}, {d_o, qb}},
-    out[] = {{dq, qb}, {dk, kb}, {dv, kb}, {delta, lb}};
+    out[] = {{dq, qb}, {dk, kb}, {dv, kb}, {use_scratch ? nullptr : delta, lb}};
   for (int i = 0; i < 4; ++i) {
     for (int j = 0; j < 6; ++j)
       if (overlaps(out[i].p, out[i].n, in[j].p, in[j].n)) return ATTN_ERR_ALIAS;
     for (int j = 0; j < i; ++j)
       if (overlaps(out[i].p, out[i].n, out[j].p, out[j].n)) return ATTN_ERR_ALIAS;
+  }
+  if (use_scratch && Nq > 0) {
+    delta = scratch_rows();
+    if (!delta) return ATTN_ERR_LAUNCH;
   }
 
   const BwdArgs a{q, k, v, o, d_o, lse, dq, dk, dv, delta, (int)BH, Nq, Nk, (int)nq, (int)nk,
@@ -640,4 +679,22 @@ extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void*
   const hipError_t err = dtype == ATTN_BF16 ? launch_bwd_type<__bf16>(a, d, causal != 0)
                                             : launch_bwd_type<_Float16>(a, d, causal != 0);
   return err == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                        const float* lse, const void* d_o, void* dq, void* dk, void* dv,
+                        float* delta, int B, int H, int Nq, int Nk, int d, int dtype,
+                        float scale, int causal, void* stream) {
+  return bwd_run(q, k, v, o, lse, d_o, dq, dk, dv, delta, false, B, H, Nq, Nk, d, dtype, scale,
+                 causal, stream);
+}
+
+extern "C" int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                                const float* lse, const void* d_o, void* dq, void* dk, void* dv,
+                                int B, int H, int Nq, int Nk, int d, int dtype, float scale,
+                                int causal, void* stream) {
+  return bwd_run(q, k, v, o, lse, d_o, dq, dk, dv, nullptr, true, B, H, Nq, Nk, d, dtype, scale,
+                 causal, stream);
 }

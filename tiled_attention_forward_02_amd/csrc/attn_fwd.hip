@@ -699,6 +699,7 @@ extern "C" const char* attn_strerror(int status) {
     case ATTN_ERR_SCALE: return "scale must be finite";
     case ATTN_ERR_LAUNCH: return "kernel launch failed";
     case ATTN_ERR_DTYPE: return "unsupported element type: ATTN_BF16 or ATTN_F16";
+    case ATTN_ERR_SCRATCH: return "attn_bwd_noalloc: B*H*Nq exceeds its static buffer (4194304 rows)";
     default: return "unknown status";
   }
 }
