@@ -13,7 +13,9 @@
 // two blocks of 32 that share every K and V fragment it reads from LDS. Two
 // (d=128), three (d=96) or four (d=64) workgroups share a CU, so each SIMD
 // holds waves of different workgroups whose softmax (VALU) and matrix (MFMA)
-// phases interleave. Keys and values
+// phases interleave. On big grids at d = 128 a separate kernel (further down)
+// runs 512-row workgroups whose two wave groups alternate the two kinds of
+// work by barrier, a phase apart. Keys and values
 // stream through LDS in tiles of 32 (d=128) or 64 (d=64) keys, double
 // buffered one tile ahead with one barrier per tile: at d = 64, 96, 128 and
 // 256 both, by buffer loads that write LDS directly (LDS DMA),
@@ -107,7 +109,8 @@ constexpr bool kVDma = D == 64 || D == 96 || D == 128 || D == 256;
 // +2.3% and +1.8% on two non-causal d = 64 shapes, +2.8% at d = 96, +1.8% at
 // d = 256, and with the bit-select mask below +1.4% on causal d = 64.
 
-// Workgroup shapes: QB 32-query blocks per wave, NW waves per workgroup.
+// Workgroup shapes: QB 32-query blocks per wave, NW waves per workgroup (the
+// 512-row shape at d = 128, QB = 2 and NW = 8, runs the ping-pong kernel).
 // d = 32, 96 and 256 have two, chosen at launch by the size of the grid:
 // eight waves of one block (256 rows) on big grids, which halves the
 // HBM -> LDS staging per FLOP, else four waves. At d = 96 (two workgroups
@@ -117,7 +120,11 @@ constexpr bool kVDma = D == 64 || D == 96 || D == 128 || D == 256;
 // A/Bs). At d = 64 eight waves gained +0.5% on big grids and
 // lost 2.6-2.8% on the two small workloads, so d = 64 keeps four. d = 128
 // has three:
-// - QB = 2, NW = 8 (512 rows a workgroup, one per CU, two waves per SIMD);
+// - QB = 2, NW = 8 (512 rows a workgroup, one per CU, two waves per SIMD),
+//   in the ping-pong kernel: +8.9% on B=16 H=16 N=4096 and +9.5% on the long
+//   causal shape over the same shape run by this kernel, whose two waves of a
+//   SIMD did the same kind of work at the same time (interleaved A/B,
+//   bit-identical outputs);
 // - QB = 2, NW = 4 (256 rows, two per CU, two waves per SIMD);
 // - QB = 1, NW = 4 (128 rows, three per CU, three waves per SIMD).
 // With two blocks a wave, every K and V^T fragment it reads from LDS serves
@@ -133,7 +140,9 @@ constexpr bool kVDma = D == 64 || D == 96 || D == 128 || D == 256;
 // Workgroups per CU the register allocation must allow.
 template <int D, int QB, int NW>
 constexpr int kMinBlocks =
-    QB == 2 ? 8 / NW : (D == 64 ? 4 : D == 96 || D == 128 ? 3 : 2) * kWaves / NW;
+    QB == 2 ? 8 / NW
+    : NW == 8 ? (D == 256 ? 1 : 2)  // eight-wave shapes: d = 32, 96 two a CU, d = 256 one
+              : (D == 64 ? 4 : D == 96 || D == 128 ? 3 : 2);
 // The most query rows a workgroup has (the 32-bit offset check on Nq allows
 // for one workgroup's rows past the end).
 constexpr int kBlockMMax = 32 * 8 * 2;
@@ -519,6 +528,373 @@ __global__ __launch_bounds__(64 * NW, (kMinBlocks<D, QB, NW>)) void attn_fwd_ker
   }
 }
 
+// ------------------------------------------ ping-pong kernel (d = 128, big grids) --
+// 512 query rows a workgroup of 8 waves, two 32-query blocks a wave; waves w
+// and w + 4 share a SIMD. Each wave alternates an MFMA phase M(t) (O^T +=
+// V^T P^T of tile t-1, then S^T = K Q^T of tile t) and a softmax phase X(t)
+// (mask, weights, row sums of tile t), with a workgroup barrier after each;
+// waves 4-7 run one phase behind waves 0-3, so on every SIMD one wave's
+// matrix work runs beside the other's softmax instead of both waves doing the
+// same kind of work at once. The MFMA phase must then keep the matrix pipe
+// fed on its own: its LDS operands are read three MFMA pairs ahead (the first
+// V^T fragments at the end of the softmax phase before, the first K
+// fragments during the last P*V pairs), and the tile DMA is issued between
+// MFMAs without a branch.
+//
+// Tiles of 32 keys, rows of 256 bytes without padding, in a ring of three
+// LDS stages (K at +0, V at +8 KiB). K keeps 16-byte chunk c of row r at
+// chunk c ^ (r & 15), so the 16 rows one pass of a 16-byte read covers hit
+// all 64 banks; V keeps 64-byte group g of row r at group g ^ (r & 3), so the
+// 4 rows one pass of a transposing read covers do. Both swizzles depend on
+// the lane only through lane / 16 and the wave, so each wave's two DMA
+// instructions of a tile part (rows 4 w' .. +3 and 16 + 4 w' .. +3,
+// w' = wave % 4) use one per-lane source offset.
+template <typename E, int D, bool CAUSAL>
+__global__ __launch_bounds__(512, 1) void attn_fwd_pp_kernel(
+    const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict__ V, E* __restrict__ O,
+    float* __restrict__ LSE, int BH, int Nq, int Nk, int nq, float c) {
+  static_assert(D == 128, "the ping-pong kernel is laid out for d = 128");
+  constexpr int QB = 2, NW = 8, NST = 3, BN = 32;
+  constexpr uint32_t ROWB = D * 2;            // bytes per row
+  constexpr uint32_t TB = BN * ROWB;          // bytes per K or V tile
+  constexpr uint32_t SB = 2 * TB;             // bytes per stage
+  typedef typename Elem<E>::v8 v8;
+  typedef typename Elem<E>::v4 v4;
+  __shared__ __attribute__((aligned(1024))) char smem[NST * SB];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, col = lane & 31, half = lane >> 5;
+  const bool late = wave >= 4;
+  const int dwave = wave & 3;
+
+  constexpr int kBlockM = 32 * NW * QB;
+  int bh, qt;
+  map_block(blockIdx.x, BH, nq, CAUSAL, bh, qt);
+  const int q0 = qt * kBlockM;
+  const int qw = q0 + 32 * QB * wave;
+  const int off = Nk - Nq;
+  const size_t qhead = (size_t)bh * (size_t)Nq * D;
+  const size_t khead = (size_t)bh * (size_t)Nk * D;
+  const uint32_t q_bytes = (uint32_t)Nq * D * 2;
+  const rsrc_t rq = make_rsrc(Q + qhead, q_bytes);
+
+  u32x4 qraw[QB][D / 16];
+#pragma unroll
+  for (int b = 0; b < QB; ++b)
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s)
+      qraw[b][s] = load16(rq, (uint32_t)((qw + 32 * b + col) * D + 16 * s + 8 * half) * 2);
+  if (c < 0.f) {
+    c = -c;
+#pragma unroll
+    for (int b = 0; b < QB; ++b)
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) qraw[b][s] ^= 0x80008000u;
+  } else if (c == 0.f) {
+    c = 1.f;
+#pragma unroll
+    for (int b = 0; b < QB; ++b)
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) qraw[b][s] = u32x4{0, 0, 0, 0};
+  }
+  v8 qf[QB][D / 16];
+#pragma unroll
+  for (int b = 0; b < QB; ++b)
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) qf[b][s] = __builtin_bit_cast(v8, qraw[b][s]);
+
+  const int kv_end = CAUSAL ? min(Nk, q0 + kBlockM + off) : Nk;
+  const int nt = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
+  // Tiles t < wave_nt hold a key this wave's rows see.
+  const int wave_kv_end = qw < Nq ? (CAUSAL ? min(Nk, qw + 32 * QB + off) : Nk) : 0;
+  const int wave_nt = wave_kv_end > 0 ? (wave_kv_end + BN - 1) / BN : 0;
+
+  const char* const lds = smem;
+  lds_char* const lds3 = to_lds(smem);
+
+  // DMA source offset of this lane (row 4 w' + lane / 16 of a 16-row half,
+  // the logical chunk its physical slot lane % 16 holds): K for the late
+  // waves, V for the early ones.
+  uint32_t dsrc;
+  {
+    const int r = 4 * dwave + (lane >> 4), pc = lane & 15;
+    const int ck = pc ^ (r & 15);
+    const int cv = 4 * ((pc >> 2) ^ (r & 3)) + (pc & 3);
+    dsrc = (uint32_t)(r * (int)ROWB + 16 * (late ? ck : cv));
+  }
+  // This wave's two DMA instructions of the K (late waves) or V (early
+  // waves) part of the tile from key k0, into the stage at byte `base`. Each
+  // 16-row half goes through a resource based at its first row whose record
+  // count ends at the head's last key (zero if the half lies past it), so
+  // rows past Nk come back as zeros.
+  auto dma = [&](uint32_t base, int k0) __attribute__((always_inline)) {
+    const E* src = late ? K : V;
+    const uint32_t part = late ? 0u : TB;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r0 = k0 + 16 * i;
+      const uint32_t n = r0 < Nk ? (uint32_t)(Nk - r0) * ROWB : 0u;
+      load16_lds(make_rsrc(src + khead + (size_t)r0 * D, n),
+                 lds3 + base + part + 1024 * (dwave + 4 * i), dsrc);
+    }
+  };
+  // Read bases: K fragment j of lane (col, half) is logical chunk 2 j + half
+  // of row col, at kb ^ 32 j; V^T fragment (rows row0 .., columns 32 db ..)
+  // at (vb ^ 64 db) + row0 * 256 (+ 8 rows for its second read).
+  const uint32_t kb = (uint32_t)(col * (int)ROWB + 16 * (half ^ (col & 15)));
+  uint32_t vb;
+  {
+    const int g = lane >> 4, s = lane & 15;
+    vb = (uint32_t)((4 * (g >> 1) + (s >> 2)) * (int)ROWB + 64 * ((s >> 2) & 3) + 32 * (g & 1) +
+                    8 * (s & 3)) + TB;
+  }
+  // The XORs are redone at each use (one VALU op each) rather than hoisted
+  // out of the loop into eight more live registers: `kbase` and `vbase` pass
+  // the bases through an empty asm once per phase, which the compiler cannot
+  // see through.
+  uint32_t kbl = kb, vbl = vb;
+  auto refresh = [&]() __attribute__((always_inline)) {
+    asm volatile("" : "+v"(kbl), "+v"(vbl));
+  };
+  auto kfrag = [&](uint32_t base, int j) __attribute__((always_inline)) {
+    return *reinterpret_cast<const v8*>(lds + base + (kbl ^ (32u * j)));
+  };
+  auto vfrag = [&](uint32_t base, int i) __attribute__((always_inline)) {
+    const int sg = i >> 2, db = i & 3;
+    const char* p = lds + base + (vbl ^ (64u * db)) + 16 * sg * ROWB;
+    const u32x2 lo = lds_read_tr16(p), hi = lds_read_tr16(p + 8 * ROWB);
+    return __builtin_bit_cast(v8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+  };
+
+  f32x16 oacc[QB][D / 32];
+#pragma unroll
+  for (int b = 0; b < QB; ++b)
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) oacc[b][db] = f32x16{};
+  float m_run[QB], l_run[QB];
+#pragma unroll
+  for (int b = 0; b < QB; ++b) {
+    m_run[b] = -FLT_MAX;
+    l_run[b] = 0.f;
+  }
+  // Weights of the last tile softmaxed (bf16), consumed by the next M phase,
+  // and the first two V^T fragments of that tile, read at the end of the
+  // softmax phase.
+  v8 pb[QB][2];
+  v8 vpre[3];
+
+  // Mask, weights and row sums of tile t (its scores in sacc) into pb. The
+  // two query blocks' weights are computed interleaved (the wave runs this
+  // phase alone on its SIMD's VALU, so it needs the independent work); each
+  // block's sum keeps its own order.
+  auto softmax = [&](f32x16 (&sacc)[QB], int t) __attribute__((always_inline)) {
+    const int k0 = t * BN;
+    if ((k0 + BN > Nk) || (CAUSAL && k0 + BN - 1 > qw + off)) {
+#pragma unroll
+      for (int b = 0; b < QB; ++b) {
+        const int qi = qw + 32 * b + col;
+        const int lim = (CAUSAL ? min(Nk - 1, qi + off) : Nk - 1) - k0 - 4 * half;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int o = 8 * (i >> 2) + (i & 3);
+          sacc[b][i] = neg_inf_where((lim - o) >> 31, sacc[b][i]);
+        }
+      }
+    }
+    float tsum[QB];
+    auto weights = [&](int b) __attribute__((always_inline)) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[b][i], c, -m_run[b]));
+        if (i == 0)
+          tsum[b] = p;
+        else
+          tsum[b] += p;
+        pb[b][i >> 3][i & 7] = (E)p;
+      }
+    };
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+#pragma unroll
+      for (int b = 0; b < QB; ++b) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[b][i], c, -m_run[b]));
+        if (i == 0)
+          tsum[b] = p;
+        else
+          tsum[b] += p;
+        pb[b][i >> 3][i & 7] = (E)p;
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < QB; ++b) {
+      if (t == 0 || __any(tsum[b] > kLazySum)) {
+        float mx = fmaxf(sacc[b][0], sacc[b][1]);
+#pragma unroll
+        for (int i = 2; i < 16; i += 2) mx = fmaxf(mx, fmaxf(sacc[b][i], sacc[b][i + 1]));
+        const float m_new = fmaxf(m_run[b], swap_halves_max(mx) * c);
+        const float alpha = __builtin_amdgcn_exp2f(m_run[b] - m_new);
+        l_run[b] *= alpha;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) oacc[b][db] *= alpha;
+        m_run[b] = m_new;
+        weights(b);
+      }
+      l_run[b] += tsum[b];
+    }
+  };
+  auto barrier = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // O^T += V^T P^T of the V tile of the stage at `base`, fragments 0 and 1
+  // already in vpre; fragment i + 2 is read while pair i runs.
+  auto pv = [&](uint32_t base, auto tail) __attribute__((always_inline)) {
+    v8 f[4] = {vpre[0], vpre[1], vpre[2], v8{}};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (i + 3 < 8) f[(i + 3) % 4] = vfrag(base, i + 3);
+      const v8 a = f[i % 4];
+      const int sg = i >> 2, db = i & 3;
+#pragma unroll
+      for (int b = 0; b < QB; ++b) oacc[b][db] = Elem<E>::mfma(a, pb[b][sg], oacc[b][db]);
+      if (i == 5) tail();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // S^T = K Q^T of the K tile of the stage at `base`, fragments 0 and 1 in
+  // g already; fragment j + 2 is read while pair j runs.
+  auto sgemm = [&](f32x16 (&sacc)[QB], uint32_t base, v8 (&g)[4], auto after0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < D / 16; ++j) {
+      if (j + 3 < D / 16) g[(j + 3) % 4] = kfrag(base, j + 3);
+      const v8 a = g[j % 4];
+#pragma unroll
+      for (int b = 0; b < QB; ++b)
+        sacc[b] = j == 0 ? Elem<E>::mfma(a, qf[b][j], f32x16{})
+                         : Elem<E>::mfma(a, qf[b][j], sacc[b]);
+      if (j == 0) {
+        __builtin_amdgcn_sched_barrier(0);
+        after0();
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // One tile t, stage st = t % 3 (phases 2t and 2t+1 for the early waves,
+  // 2t+1 and 2t+2 for the late ones):
+  //  M(t): O += P*V of tile t-1, then S of tile t. Between the two (after
+  //        the transposing reads, which would otherwise wait for it) the
+  //        early waves issue V of tile t+1 (its stage last read in the phase
+  //        before), the late waves K of tile t+2 (into the stage of tile
+  //        t-1, whose K part was last read two phases before).
+  //  X(t): softmax of tile t into pb; read the first V^T fragments of tile t
+  //        for the next M phase; wait for this wave's DMA, one phase or more
+  //        before the first read of what it loaded.
+  auto body = [&](int t, auto st_c, auto first_c) __attribute__((always_inline)) {
+    constexpr int st = decltype(st_c)::value;
+    constexpr bool first = decltype(first_c)::value;
+    constexpr uint32_t bcur = st * SB, bprev = ((st + 2) % NST) * SB;
+    constexpr uint32_t bnext = ((st + 1) % NST) * SB;
+    const bool do_s = t < wave_nt;
+    refresh();
+    __builtin_amdgcn_s_setprio(1);
+    // The first three K fragments of tile t are read while the last P*V
+    // pairs run (always: the stage holds tile t either way).
+    v8 g[4];
+    auto kread = [&]() __attribute__((always_inline)) {
+#pragma unroll
+      for (int j = 0; j < 3; ++j) g[j] = kfrag(bcur, j);
+    };
+    // P*V of tile t-1 runs for every wave: one that skipped that tile holds
+    // zero weights and adds exact zeros (its V rows are real data, or zeros
+    // past the end). The first tile has no predecessor.
+    if constexpr (first) {
+      kread();
+    } else {
+      pv(bprev, kread);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // The early waves load V of tile t+1 into the next stage, the late ones K
+    // of tile t+2 into the previous one; issued without a branch (a tile past
+    // the last one is loaded as zeros into a stage nobody reads again), after
+    // the first S pair so that the matrix pipe has work meanwhile.
+    auto issue_dma = [&]() __attribute__((always_inline)) {
+      dma(late ? bprev : bnext, (t + (late ? 2 : 1)) * BN);
+    };
+    f32x16 sacc[QB];
+    if (do_s) {
+      sgemm(sacc, bcur, g, issue_dma);
+    } else {
+      issue_dma();
+    }
+    __builtin_amdgcn_s_setprio(0);
+    barrier();
+    if (do_s) {
+      softmax(sacc, t);
+    } else {
+#pragma unroll
+      for (int b = 0; b < QB; ++b) pb[b][0] = pb[b][1] = v8{};
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    refresh();
+#pragma unroll
+    for (int i = 0; i < 3; ++i) vpre[i] = vfrag(bcur, i);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's DMA
+    barrier();
+  };
+
+  // Prologue: V of tile 0 by the early waves, K of tiles 0 and 1 by the
+  // late ones (in M(0) the early waves load V of tile 1, the late ones K of
+  // tile 2); the late waves then wait one extra barrier, which puts them one
+  // phase behind.
+  if (nt > 0) dma(0, 0);
+  if (late && nt > 1) dma(SB, BN);
+  __builtin_amdgcn_s_waitcnt(0);
+  barrier();
+  if (late) barrier();
+  using no = std::false_type;
+  if (nt > 0) body(0, std::integral_constant<int, 0>{}, std::true_type{});
+  for (int t = 1; t < nt; t += 3) {
+    body(t, std::integral_constant<int, 1>{}, no{});
+    if (t + 1 < nt) body(t + 1, std::integral_constant<int, 2>{}, no{});
+    if (t + 2 < nt) body(t + 2, std::integral_constant<int, 0>{}, no{});
+  }
+  // P*V of the last tile; the early waves then wait at the barrier that
+  // evens the counts.
+  if (nt >= 1 && nt - 1 < wave_nt) {
+    __builtin_amdgcn_s_setprio(1);
+    pv(((nt - 1) % NST) * SB, []() {});
+    __builtin_amdgcn_s_setprio(0);
+  }
+  if (!late) barrier();
+
+  const rsrc_t ro = make_rsrc(O + qhead, q_bytes);
+  const rsrc_t rl = make_rsrc(LSE + (size_t)bh * Nq, (uint32_t)Nq * 4);
+#pragma unroll
+  for (int b = 0; b < QB; ++b) {
+    const int qi = qw + 32 * b + col;
+    const float total = swap_halves_add(l_run[b]);
+    const float inv = total > 0.f ? 1.0f / total : 0.f;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        v4 o4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o4[e] = (E)(oacc[b][db][4 * r + e] * inv);
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, o4), ro,
+                                              (int)((qi * D + 32 * db + 8 * r + 4 * half) * 2),
+                                              0, 0);
+      }
+    }
+    if (half == 0) {
+      const float lse = total > 0.f ? (m_run[b] + log2f(total)) * kLn2 : -INFINITY;
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lse), rl, qi * 4, 0, 0);
+    }
+  }
+}
+
 // ------------------------------------------------------------- host side --
 
 struct Shape {
@@ -533,6 +909,8 @@ void tile_info(Shape* sh) {
 }
 
 constexpr int64_t kCUs = 256;  // gfx950 parts have 256 CUs
+// LDS of the ping-pong kernel: three stages of a 32-key K and V tile at d = 128.
+constexpr int kPingPongLds = 3 * 2 * 32 * 128 * 2;
 
 // The workgroup shape at d = 128: the largest whose grid still gives every CU
 // two workgroups' worth of rows (512-row workgroups: two rounds of one per
@@ -576,6 +954,7 @@ int check_sizes(int B, int H, int Nq, int Nk, int d, Shape* sh) {
   if (d == 32 || d == 96 || d == 256) sh->nw = pick_waves_one_block((int64_t)B * H, Nq, d);
   sh->block = 64 * sh->nw;
   sh->block_m = 32 * sh->nw * sh->qb;
+  if (d == 128 && sh->qb == 2 && sh->nw == 8) sh->lds = kPingPongLds;
   const int64_t nq = ((int64_t)Nq + sh->block_m - 1) / sh->block_m;
   const int64_t grid = (int64_t)B * H * nq;
   if (grid > INT32_MAX) return ATTN_ERR_SHAPE;
@@ -599,6 +978,20 @@ struct Args {
   hipStream_t stream;
 };
 
+template <typename E, int D, bool CAUSAL>
+hipError_t launch_pp(const Shape& sh, const Args& a) {
+  const E* qp = static_cast<const E*>(a.q);
+  const E* kp = static_cast<const E*>(a.k);
+  const E* vp = static_cast<const E*>(a.v);
+  E* op = static_cast<E*>(a.o);
+  float* lp = a.lse;
+  int BH = a.BH, Nq = a.Nq, Nk = a.Nk, nq = sh.nq;
+  float c = a.c;
+  void* args[] = {&qp, &kp, &vp, &op, &lp, &BH, &Nq, &Nk, &nq, &c};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&attn_fwd_pp_kernel<E, D, CAUSAL>),
+                         dim3(sh.grid), dim3(sh.block), args, 0, a.stream);
+}
+
 template <typename E, int D, bool CAUSAL, int QB, int NW>
 hipError_t launch(const Shape& sh, const Args& a) {
   const E* qp = static_cast<const E*>(a.q);
@@ -619,7 +1012,7 @@ hipError_t launch_shape(const Shape& sh, const Args& a) {
     if (sh.nw == 8) return launch<E, D, CAUSAL, 1, 8>(sh, a);
   }
   if constexpr (D == 128) {
-    if (sh.qb == 2 && sh.nw == 8) return launch<E, D, CAUSAL, 2, 8>(sh, a);
+    if (sh.qb == 2 && sh.nw == 8) return launch_pp<E, D, CAUSAL>(sh, a);
     if (sh.qb == 2) return launch<E, D, CAUSAL, 2, 4>(sh, a);
   }
   return launch<E, D, CAUSAL, 1, kWaves>(sh, a);
