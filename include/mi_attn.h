@@ -191,9 +191,10 @@ const char* attn_strerror(int status);
  * attn_fwd_launch_shape - the launch attn_fwd would make for these sizes,
  * without launching: workgroups in the 1-D grid, threads per workgroup, LDS
  * bytes per workgroup, query rows per workgroup (block_m) and keys per inner
- * step (block_n). At every d but 64 the workgroup shape depends on the grid:
- * bigger workgroups (256 query rows in 512 threads, or at d = 128 up to 512
- * rows) when B, H and N still give every CU enough of them. Out-params may
+ * step (block_n). The workgroup shape depends on the grid: bigger
+ * workgroups (256 query rows in 512 threads, or at d = 64 and 128 512 rows)
+ * when B, H and N still give every CU enough of them (at d = 64 also only
+ * when N >= 4096). Out-params may
  * not be NULL. Returns the same validation
  * status attn_fwd would for the sizes (pointers are not examined); on error
  * the out-params are untouched. For B*H*N == 0 it returns ATTN_OK with

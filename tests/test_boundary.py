@@ -357,8 +357,22 @@ def test_launch_shape_d128_follows_the_grid(lib, B, H, N, rows):
     assert s["block_m"] == rows
     assert s["block"] == (512 if rows == 512 else 256)
     assert s["grid"] == B * H * ((N + rows - 1) // rows)
-    # other head dims keep 128 rows and four waves
-    assert mi.attn_fwd_launch_shape(B, H, N, 64, False)["block_m"] == 128
+
+
+@pytest.mark.parametrize("B,H,N,rows", [(16, 16, 4096, 512), (1, 32, 16384, 512),
+                                        (4, 16, 4100, 512), (2, 16, 4096, 128),
+                                        (8, 16, 2048, 128), (4, 16, 1024, 128),
+                                        (64, 16, 4095, 128)])
+def test_launch_shape_d64_follows_the_grid_and_the_rows(lib, B, H, N, rows):
+    # d = 64 takes the 512-row workgroups (eight waves, 48 KiB of LDS) only when
+    # both axes have at least 4096 rows and the grid gives every CU two of them
+    s = mi.attn_fwd_launch_shape(B, H, N, 64, True)
+    assert s["block_m"] == rows
+    assert s["block"] == (512 if rows == 512 else 256)
+    assert s["block_n"] == 64
+    assert s["grid"] == B * H * ((N + rows - 1) // rows)
+    if rows == 512:
+        assert s["lds_bytes"] == 3 * 2 * 8192
 
 
 @pytest.mark.parametrize("B,H,N,rows", [(16, 16, 4096, 256), (1, 32, 16384, 256),
