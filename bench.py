@@ -59,7 +59,8 @@ PKG = os.path.join(ROOT, "tiled_attention_forward_02_amd")
 # The files each timed pass is built from, its compile flags included (hashed
 # to tie profiles to code).
 KERNEL_SRCS = {"fwd": ("csrc/attn_fwd.hip", "csrc/common.h", "build.py"),
-               "bwd": ("csrc/attn_bwd.hip", "csrc/common.h", "build.py")}
+               "bwd": ("csrc/attn_bwd.hip", "csrc/attn_bwd_kernels.h", "csrc/attn_bwd256.hip",
+                       "csrc/common.h", "build.py")}
 PROFILES = os.path.join(ROOT, "profiles")
 
 

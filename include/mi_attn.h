@@ -32,7 +32,7 @@ typedef enum {
   ATTN_OK = 0,
   ATTN_ERR_NULL = -1,      /* a required pointer (q, k, v, o, lse, or an out-param) is NULL */
   ATTN_ERR_SHAPE = -2,     /* a size is negative, or one head (N*d*2 bytes) reaches 2^31 */
-  ATTN_ERR_HEADDIM = -3,   /* d is not one of 32, 64, 96, 128, 256 (attn_bwd: not 256) */
+  ATTN_ERR_HEADDIM = -3,   /* d is not one of 32, 64, 96, 128, 256 */
   ATTN_ERR_ALIGN = -5,     /* q, k, v or o not 16-byte aligned, or lse not 4-byte aligned */
   ATTN_ERR_ALIAS = -6,     /* o or lse overlaps an input, or o overlaps lse */
   ATTN_ERR_SCALE = -7,     /* scale is NaN or infinite */
@@ -138,8 +138,8 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse
  *   dq        [B, H, Nq, d]; dk, dv [B, H, Nk, d]; written, every element.
  *   delta     float32 [B, H, Nq], caller-owned; receives D_i (the first kernel
  *             the call queues writes it, a later one reads it back).
- *   B, H, Nq, Nk, d, dtype, scale, causal, stream: as for attn_fwd_ex, except
- *             that d must be 32, 64, 96 or 128.
+ *   B, H, Nq, Nk, d, dtype, scale, causal, stream: as for attn_fwd_ex (d is
+ *             32, 64, 96, 128 or 256).
  *
  * All tensors are contiguous row-major in the element type `dtype` (delta and
  * lse float32). Arithmetic: products of the element type accumulated in fp32;

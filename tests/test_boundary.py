@@ -264,7 +264,7 @@ def bwd(lib, d=128, dtype=0, B=2, H=3, Nq=100, Nk=70, scale=0.125, causal=0, **p
                         p["dv"], p["delta"], B, H, Nq, Nk, d, dtype, scale, causal, None)
 
 
-@pytest.mark.parametrize("d", [0, 16, 48, 80, 256, 512])
+@pytest.mark.parametrize("d", [0, 16, 48, 80, 255, 512])
 def test_bwd_head_dims(lib, d):
     assert bwd(lib, d=d) == ERR_HEADDIM
 
@@ -305,7 +305,7 @@ def bwd_noalloc(lib, d=128, dtype=0, B=2, H=3, Nq=100, Nk=70, scale=0.125, causa
 def test_bwd_noalloc_validates_like_attn_bwd(lib):
     """Every argument check of attn_bwd, without the delta argument; all of
     them come before the one-time lookup of the static buffer."""
-    for d in (0, 16, 256):
+    for d in (0, 16, 257):
         assert bwd_noalloc(lib, d=d) == ERR_HEADDIM
     assert bwd_noalloc(lib, dtype=2) == ERR_DTYPE
     assert bwd_noalloc(lib, scale=float("inf")) == ERR_SCALE

@@ -95,7 +95,7 @@ def check_all(q, k, v, do, scale, causal, what):
 RAGGED = [(1, 1, 1), (1, 2, 17), (2, 3, 100), (1, 1, 129), (2, 2, 300), (1, 3, 513)]
 
 
-@pytest.mark.parametrize("d", [32, 64, 96, 128])
+@pytest.mark.parametrize("d", [32, 64, 96, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("B,H,N", RAGGED)
 def test_bwd_ragged(B, H, N, d, causal):
@@ -108,7 +108,7 @@ def test_bwd_ragged(B, H, N, d, causal):
 CROSS = [(3, 2), (2, 3), (100, 37), (37, 100), (129, 1000), (1000, 129), (200, 1), (1, 200)]
 
 
-@pytest.mark.parametrize("d", [32, 64, 96, 128])
+@pytest.mark.parametrize("d", [32, 64, 96, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("Nq,Nk", CROSS)
 def test_bwd_cross(Nq, Nk, d, causal):
@@ -120,7 +120,7 @@ def test_bwd_cross(Nq, Nk, d, causal):
     check_all(qi["q"], ki["k"], ki["v"], do, qi["scale"], causal, f"cross {Nq}x{Nk}")
 
 
-@pytest.mark.parametrize("d", [32, 64, 96, 128])
+@pytest.mark.parametrize("d", [32, 64, 96, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("N", [100, 300])
 def test_bwd_fp16(N, d, causal):
@@ -151,7 +151,7 @@ def test_bwd_other_scales(scale, causal):
 
 # --------------------------------------------------------------- edge cases --
 
-@pytest.mark.parametrize("d", [32, 64, 96, 128])
+@pytest.mark.parametrize("d", [32, 64, 96, 128, 256])
 def test_bwd_longest_key_axis(d):
     """Gradients on the longest key axis one head may have (K, V, dK, dV
     2 GiB each), checked by closed forms, since the oracle cannot hold these
@@ -383,7 +383,7 @@ def test_bwd_long_causal():
     assert gap <= 1e-2 * max(np.abs(dv64).sum(axis=2).max(), np.abs(do64).sum(axis=2).max())
 
 
-@pytest.mark.parametrize("d", [32, 64, 96, 128])
+@pytest.mark.parametrize("d", [32, 64, 96, 128, 256])
 def test_bwd_long_other_head_dims(d):
     """N = 4096 at every head dim the backward takes, with and without the
     causal mask: two heads' every gradient element against the oracle, at

@@ -258,7 +258,7 @@ def attn_bwd(q, k, v, o, lse, do, scale=None, causal=False, dq=None, dk=None, dv
     scale, causal) are passed in (the forward's own outputs for these inputs).
 
     q, o, do [B, H, Nq, d] and k, v [B, H, Nk, d] share one element type
-    (bf16 or fp16); lse is float32 [B, H, Nq]; d is 32, 64, 96 or 128. ``delta``
+    (bf16 or fp16); lse is float32 [B, H, Nq]; d is 32, 64, 96, 128 or 256. ``delta``
     (float32 [B, H, Nq]) receives sum(do * o) per row and is allocated when
     not given; dq, dk, dv may be given to write into. Queued on ``stream``
     (default: torch's current stream of q's device); nothing synchronises.

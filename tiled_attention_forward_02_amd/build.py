@@ -20,10 +20,13 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 # keeps two fp32 accumulators and the K, V fragments live; left to its
 # heuristics the compiler gives its MFMAs accumulators in AGPRs and copies
 # them to VGPRs and back on every loop iteration, so the VGPR form is forced
-# there (the forward is unaffected: it is compiled on its own).
+# there (the forward is unaffected: it is compiled on its own). At d = 256
+# those accumulators need the AGPRs (they exceed the 256 VGPRs), so the d = 256
+# backward is a translation unit of its own, built without the flag.
 SOURCES = (
     ("attn_fwd.hip", ()),
     ("attn_bwd.hip", ("-mllvm", "-amdgpu-mfma-vgpr-form=1")),
+    ("attn_bwd256.hip", ()),
 )
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG_DIR, "libmi_attn.so")

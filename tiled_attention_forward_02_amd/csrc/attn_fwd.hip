@@ -1118,7 +1118,7 @@ extern "C" const char* attn_strerror(int status) {
     case ATTN_OK: return "success";
     case ATTN_ERR_NULL: return "null pointer argument";
     case ATTN_ERR_SHAPE: return "invalid shape: sizes must be >= 0 and fit 32-bit head offsets";
-    case ATTN_ERR_HEADDIM: return "unsupported head dimension: d must be 32, 64, 96, 128 or 256 (attn_bwd: not 256)";
+    case ATTN_ERR_HEADDIM: return "unsupported head dimension: d must be 32, 64, 96, 128 or 256";
     case ATTN_ERR_ALIGN: return "misaligned pointer: q, k, v, o need 16 bytes, lse 4 bytes";
     case ATTN_ERR_ALIAS: return "output buffer overlaps an input or the other output";
     case ATTN_ERR_SCALE: return "scale must be finite";
