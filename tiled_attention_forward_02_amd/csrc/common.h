@@ -158,8 +158,9 @@ struct DmaTile {
 // head dimension DL. The 64-bank LDS serves 32 lanes of an 8-byte read at a
 // time; those lanes cover 4 consecutive rows x 64 bytes, conflict-free when
 // the rows start an odd multiple of 64 bytes apart (VS = 32 mod 64). At
-// DL = 64 that pitch (96) would keep four workgroups from fitting in LDS, so
-// it stays at 80 (those reads take two passes).
+// DL = 64 that pitch (96) would keep four workgroups from fitting in LDS; the
+// forward lays d = 64 tiles out unpadded and swizzled instead, and 80 remains
+// only this function's answer for it.
 template <int DL>
 constexpr int tr_pitch() {
   return DL == 64 ? 80 : (DL % 64 == 32 ? DL : DL + 32);
