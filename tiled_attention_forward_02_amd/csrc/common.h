@@ -170,7 +170,14 @@ constexpr int tr_pitch() {
 // the address of 4 consecutive elements (8 bytes). Within each group of 16
 // lanes, lane 4a + b receives, as its element e, element b of the 4 given by
 // lane a + 4e of the group (checked on gfx950 with a layout probe).
-__device__ __forceinline__ u32x2 lds_read_tr16(const char* p) {
+//
+// `p` is restrict so that the read carries alias-scope metadata once inlined.
+// Without it, the compiler puts a vmcnt(0) before every transposing read
+// while any LDS DMA is in flight. That includes the DMA of a later tile into
+// another stage, so a tile's P*V would wait for the next tile's loads. Plain
+// LDS reads get no such wait, and neither now do these. Every kernel here
+// orders its DMA'd tiles by its own vmcnt wait and barrier before any read.
+__device__ __forceinline__ u32x2 lds_read_tr16(const char* __restrict__ p) {
   typedef short s16x4 __attribute__((ext_vector_type(4)));
   const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (__attribute__((address_space(3))) s16x4*)(p));
