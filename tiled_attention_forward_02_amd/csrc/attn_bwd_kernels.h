@@ -315,6 +315,224 @@ __global__ __launch_bounds__(64 * NW, (kBwdMinBlocks<D, NW>)) void attn_bwd_dq_k
     }
 }
 
+// --------------------------------------------- dQ ping-pong kernel (d = 128) --
+// The eight-wave shape at d = 128 without the causal mask: 256 queries a
+// workgroup, 32 a wave, one workgroup a CU; waves w and w + 4 share a SIMD.
+// Each wave alternates an MFMA phase M(t) (dQ^T += K^T dS^T of key tile
+// t-1, then S^T = K Q^T and dP^T = V dO^T of tile t) and a VALU phase X(t)
+// (P and dS of tile t), with a workgroup barrier after each; waves 4-7 run
+// one phase behind waves 0-3, so on every SIMD one wave's MFMAs run beside
+// the other's VALU work (in step, both waves of a SIMD issued MFMAs at the
+// same time and then both their VALU work).
+//
+// A key tile's K is read from the phase that computes its S until the one
+// that adds its dQ, four phases, so the tiles go round a ring of four LDS
+// stages. Tile t + 2 is loaded during M(t): K by waves 0-3, V by waves 4-7,
+// three DMA instructions a wave (each part is padded from ten instructions
+// to twelve, the last two writing zeros past the rows, so no wave
+// branches). Operands are read three MFMAs ahead.
+template <typename E, bool CAUSAL>
+__global__ __launch_bounds__(512, 1) void attn_bwd_dq_pp_kernel(
+    const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict__ V,
+    const E* __restrict__ O, const float* __restrict__ LSE, const E* __restrict__ dO,
+    E* __restrict__ dQ, float* __restrict__ Delta, int BH, int Nq, int Nk, int nq, float c,
+    float dq_scale) {
+  static_assert(!CAUSAL, "the ping-pong dQ kernel runs without the causal mask");
+  constexpr int D = 128, NW = 8, BN = 32, NST = 4, PD = 3;
+  using G = SwzTile<D, BN, NW>;  // layout and reads of a tile part
+  using GD = SwzTile<D, BN, 4>;  // its DMA, dealt to four waves
+  static_assert(GD::NINSTR == 10 && GD::NW == 3, "three DMA instructions a wave per part");
+  constexpr int PART = 12 * 1024;  // ten instructions of rows, two of padding
+  constexpr int V_OFF = PART, STAGE = 2 * PART;
+  typedef typename Elem<E>::v8 v8;
+  typedef typename Elem<E>::v4 v4;
+  __shared__ __attribute__((aligned(1024))) char smem[NST * STAGE];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, col = lane & 31, half = lane >> 5;
+  const bool late = wave >= 4;
+  const int dwave = wave & 3;
+  int bh, qt;
+  map_block(blockIdx.x, BH, nq, CAUSAL, bh, qt);
+  const int q0 = qt * 32 * NW;
+  const int qi = q0 + 32 * wave + col;
+
+  const size_t qhead = (size_t)bh * (size_t)Nq * D;
+  const size_t khead = (size_t)bh * (size_t)Nk * D;
+  const uint32_t q_bytes = (uint32_t)Nq * D * 2;
+  const uint32_t k_bytes = (uint32_t)Nk * D * 2;
+  // This wave's DMA part: K (waves 0-3) or V (waves 4-7).
+  const rsrc_t rpart = make_rsrc((late ? V : K) + khead, k_bytes);
+  const uint32_t part_off = late ? (uint32_t)V_OFF : 0u;
+
+  // Q^T and dO^T fragments (B operands, a query per lane), and D_i from this
+  // lane's half of the row of dO * O, both halves combined.
+  v8 qf[D / 16], df[D / 16];
+  float dpart = 0.f;
+  {
+    const rsrc_t rq = make_rsrc(Q + qhead, q_bytes);
+    const rsrc_t rdo = make_rsrc(dO + qhead, q_bytes);
+    const rsrc_t ro = make_rsrc(O + qhead, q_bytes);
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      const uint32_t at = (uint32_t)(qi * D + 16 * s + 8 * half) * 2;
+      qf[s] = __builtin_bit_cast(v8, load16(rq, at));
+      df[s] = __builtin_bit_cast(v8, load16(rdo, at));
+      const v8 o8 = __builtin_bit_cast(v8, load16(ro, at));
+#pragma unroll
+      for (int j = 0; j < 8; ++j) dpart = fmaf((float)df[s][j], (float)o8[j], dpart);
+    }
+  }
+  const float delta = swap_halves_add(dpart);
+  const rsrc_t rl = make_rsrc(LSE + (size_t)bh * Nq, (uint32_t)Nq * 4);
+  const float l2 = lse_log2(
+      __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rl, qi * 4, 0, 0)), qi < Nq);
+  if (half == 0) {
+    const rsrc_t rd = make_rsrc(Delta + (size_t)bh * Nq, (uint32_t)Nq * 4);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(delta), rd, qi * 4, 0, 0);
+  }
+  const int nt = Nk > 0 ? (Nk + BN - 1) / BN : 0;
+
+  const G tile(wave, lane);
+  const GD dtile(dwave, lane);
+  const char* const lds = smem;
+  lds_char* const lds3 = to_lds(smem);
+  auto dma = [&](uint32_t base, int k0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < GD::NW; ++i)
+      load16_lds(rpart, lds3 + base + part_off + 1024 * (dwave + 4 * i),
+                 dtile.off[i] + (uint32_t)k0 * D * 2);
+  };
+
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
+  // dS of the last tile (the B operand of dQ), and the first operands of the
+  // next MFMA phase, read at the end of the VALU phase.
+  v8 dsb[2];
+  v8 pre[PD];
+
+  // MFMA k of an MFMA phase: k < 8 adds tile t-1's dQ (16-key slice k / 4,
+  // output columns 32 (k % 4)); k >= 8 adds step (k - 8) / 2 of tile t's S
+  // (even) or dP (odd).
+  auto operand = [&](uint32_t bprev, uint32_t bcur, int k) __attribute__((always_inline)) {
+    if (k < 8) return tile.template cols<v8>(lds + bprev, 16 * (k / 4), 32 * (k % 4));
+    const int j = (k - 8) / 2;
+    return tile.template rows<v8>(lds + bcur + ((k & 1) ? V_OFF : 0), 0, j);
+  };
+  auto barrier = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // One tile t in stage st = t % 4 (phases 2t and 2t + 1 for waves 0-3,
+  // 2t + 1 and 2t + 2 for waves 4-7).
+  auto body = [&](int t, auto st_c, auto first_c) __attribute__((always_inline)) {
+    constexpr int st = decltype(st_c)::value;
+    constexpr bool first = decltype(first_c)::value;
+    constexpr uint32_t bcur = st * STAGE, bprev = ((st + 3) % NST) * STAGE;
+    constexpr uint32_t bload = ((st + 2) % NST) * STAGE;
+    constexpr int k_begin = first ? 8 : 0;
+    f32x16 sacc = f32x16{}, pacc = f32x16{};
+    v8 f[PD + 1];
+#pragma unroll
+    for (int i = 0; i < PD; ++i) f[i] = first ? operand(bprev, bcur, k_begin + i) : pre[i];
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int k = k_begin; k < 24; ++k) {
+      if (k + PD < 24) f[(k - k_begin + PD) % (PD + 1)] = operand(bprev, bcur, k + PD);
+      const v8 a = f[(k - k_begin) % (PD + 1)];
+      if (k < 8) {
+        acc[k % 4] = Elem<E>::mfma(a, dsb[k / 4], acc[k % 4]);
+      } else {
+        const int j = (k - 8) / 2;
+        if (k & 1)
+          pacc = Elem<E>::mfma(a, df[j], pacc);
+        else
+          sacc = Elem<E>::mfma(a, qf[j], sacc);
+      }
+      // Tile t + 2 (zeros past Nk) into the stage tile t - 2 left, after the
+      // first S step.
+      if (k == 9) {
+        __builtin_amdgcn_sched_barrier(0);
+        dma(bload, (t + 2) * BN);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __builtin_amdgcn_s_setprio(0);
+    barrier();
+    // P = 2^(s c - lse), 0 for keys past Nk, and dS^T = P^T (dP^T - D).
+    const int k0 = t * BN;
+    float p[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) p[i] = weight(sacc[i], c, l2);
+    if (k0 + BN > Nk) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = k0 + 8 * (i >> 2) + 4 * half + (i & 3);
+        if (key >= Nk) p[i] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dsb[i >> 3][i & 7] = (E)(p[i] * (pacc[i] - delta));
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < PD; ++i) pre[i] = operand(bcur, 0, i);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's DMA
+    barrier();
+  };
+
+  // Prologue: tiles 0 and 1 (K by waves 0-3, V by waves 4-7); waves 4-7
+  // then pass one extra barrier, which puts them one phase behind.
+  if (nt > 0) {
+    dma(0, 0);
+    dma(STAGE, BN);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  barrier();
+  if (late) barrier();
+  using no = std::false_type;
+  if (nt > 0) body(0, std::integral_constant<int, 0>{}, std::true_type{});
+  for (int t = 1; t < nt; t += 4) {
+    body(t, std::integral_constant<int, 1>{}, no{});
+    if (t + 1 < nt) body(t + 1, std::integral_constant<int, 2>{}, no{});
+    if (t + 2 < nt) body(t + 2, std::integral_constant<int, 3>{}, no{});
+    if (t + 3 < nt) body(t + 3, std::integral_constant<int, 0>{}, no{});
+  }
+  // dQ of the last tile; waves 0-3 then pass the barrier that evens the
+  // counts.
+  if (nt > 0) {
+    const uint32_t blast = (uint32_t)((nt - 1) % NST) * STAGE;
+    v8 f[PD + 1];
+#pragma unroll
+    for (int i = 0; i < PD; ++i) f[i] = pre[i];
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      if (k + PD < 8) f[(k + PD) % (PD + 1)] = operand(blast, 0, k + PD);
+      acc[k % 4] = Elem<E>::mfma(f[k % (PD + 1)], dsb[k / 4], acc[k % 4]);
+    }
+    __builtin_amdgcn_s_setprio(0);
+  }
+  if (!late) barrier();
+
+  // dQ = scale * acc; rows past Nq are dropped by the range check.
+  const rsrc_t rdq = make_rsrc(dQ + qhead, q_bytes);
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      v4 o4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o4[e] = (E)(acc[db][4 * r + e] * dq_scale);
+      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, o4), rdq,
+                                            (int)((qi * D + 32 * db + 8 * r + 4 * half) * 2),
+                                            0, 0);
+    }
+}
+
 // ---------------------------------------------------------- dK/dV kernel --
 
 // One pass accumulates both dK and dV: the K and V fragments and the two
@@ -545,9 +763,12 @@ hipError_t launch_bwd(const BwdArgs& a) {
   // dQ (and D) first: the key-side kernel reads D.
   if (nq > 0) {
     void* args[] = {&q, &k, &v, &o, &lse, &d_o, &dq, &delta, &BH, &Nq, &Nk, &nq, &c, &scale};
-    const hipError_t err =
-        hipLaunchKernel(reinterpret_cast<const void*>(&attn_bwd_dq_kernel<E, D, CAUSAL, NW>),
-                        dim3(BH * nq), dim3(64 * NW), args, 0, a.stream);
+    const void* fn;
+    if constexpr (D == 128 && NW == 8 && !CAUSAL)
+      fn = reinterpret_cast<const void*>(&attn_bwd_dq_pp_kernel<E, CAUSAL>);
+    else
+      fn = reinterpret_cast<const void*>(&attn_bwd_dq_kernel<E, D, CAUSAL, NW>);
+    const hipError_t err = hipLaunchKernel(fn, dim3(BH * nq), dim3(64 * NW), args, 0, a.stream);
     if (err != hipSuccess) return err;
   }
   if (nk > 0) {
