@@ -110,14 +110,16 @@ constexpr bool kVDma = D == 64 || D == 96 || D == 128 || D == 256;
 // d = 256, and with the bit-select mask below +1.4% on causal d = 64.
 
 // Workgroup shapes: QB 32-query blocks per wave, NW waves per workgroup (the
-// 512-row shape at d = 128, QB = 2 and NW = 8, runs the ping-pong kernel).
+// 512-row shape at d = 128, QB = 2 and NW = 8, and the 256-row shape at
+// d = 256 run the ping-pong kernel).
 // d = 32, 96 and 256 have two, chosen at launch by the size of the grid:
 // eight waves of one block (256 rows) on big grids, which halves the
 // HBM -> LDS staging per FLOP, else four waves. At d = 96 (two workgroups
 // per CU, four waves per SIMD) that gave +2.7% on B=16 H=16 N=4096 and +3.4%
 // on the long causal shape, at d = 256 (one per CU, two waves per SIMD)
 // +3.9% and +6.7%, at d = 32 (two per CU) +3.5% and +2.3% (interleaved
-// A/Bs). At d = 64 eight waves gained +0.5% on big grids and
+// A/Bs). At d = 256 the ping-pong kernel then ran those eight waves 1.9% and
+// 2.7% faster than this kernel. At d = 64 eight waves gained +0.5% on big grids and
 // lost 2.6-2.8% on the two small workloads, so d = 64 keeps four. d = 128
 // has three:
 // - QB = 2, NW = 8 (512 rows a workgroup, one per CU, two waves per SIMD),
@@ -575,35 +577,39 @@ __global__ __launch_bounds__(64 * NW, (kMinBlocks<D, QB, NW>)) void attn_fwd_ker
   }
 }
 
-// ---------------------------------- ping-pong kernel (d = 64 and 128, big grids) --
-// 512 query rows a workgroup of 8 waves, two 32-query blocks a wave; waves w
-// and w + 4 share a SIMD. Each wave alternates an MFMA phase M(t) (O^T +=
-// V^T P^T of tile t-1, then S^T = K Q^T of tile t) and a softmax phase X(t)
-// (mask, weights, row sums of tile t), with a workgroup barrier after each;
-// waves 4-7 run one phase behind waves 0-3, so on every SIMD one wave's
-// matrix work runs beside the other's softmax instead of both waves doing the
-// same kind of work at once. The MFMA phase must then keep the matrix pipe
-// fed on its own: its LDS operands are read three MFMA pairs ahead (the first
-// V^T fragments at the end of the softmax phase before, the first K
-// fragments during the last P*V pairs), and the tile DMA is issued between
-// MFMAs without a branch.
+// ------------------------------ ping-pong kernel (d = 64, 128 and 256, big grids) --
+// 512 query rows a workgroup of 8 waves, two 32-query blocks a wave (256 rows,
+// one block a wave, at d = 256); waves w and w + 4 share a SIMD. Each wave
+// alternates an MFMA phase M(t) (O^T += V^T P^T of tile t-1, then
+// S^T = K Q^T of tile t) and a softmax phase X(t) (mask, weights, row sums of
+// tile t), with a workgroup barrier after each; waves 4-7 run one phase
+// behind waves 0-3, so on every SIMD one wave's matrix work runs beside the
+// other's softmax instead of both waves doing the same kind of work at once.
+// The MFMA phase must then keep the matrix pipe fed on its own: its LDS
+// operands are read three MFMAs ahead (the first fragments of M(t+1) at the
+// end of X(t), the first K fragments during the last P*V MFMAs), and the tile
+// DMA is issued between MFMAs without a branch. At d = 256 a wave's one S
+// chain of 16 dependent MFMAs would stall the pipe, so its steps alternate
+// with the P*V MFMAs.
 //
-// Tiles of 8 KiB of K and 8 of V (32 keys at d = 128, 64 at d = 64), rows
-// without padding, in a ring of three LDS stages (K at +0, V at +8 KiB). K
-// keeps 16-byte chunk c of row r at chunk c ^ (r & 15) (d = 128) or
-// c ^ ((r >> 1) & 7) (d = 64), so the 16 rows one pass of a 16-byte read
-// covers hit all 64 banks; V keeps 64-byte group g of row r at g ^ (r & 3)
-// (d = 128) or g ^ ((r >> 1) & 1) (d = 64), so the 4 rows one pass of a
-// transposing read covers do. Both swizzles depend on the lane only through
-// lane / 16 and the wave, so each wave's two DMA instructions of a tile part
-// (one per half tile) use one per-lane source offset.
+// Tiles of 8 KiB of K and 8 of V (32 keys at d = 128, 64 at d = 64; 16 KiB
+// each of 32 keys at d = 256), rows without padding, in a ring of three LDS
+// stages (K at +0, V after it). K keeps 16-byte chunk c of row r at chunk
+// c ^ (r & 15) (d >= 128) or c ^ ((r >> 1) & 7) (d = 64), so the 16 rows one
+// pass of a 16-byte read covers hit all 64 banks (rows 256 or 512 bytes
+// apart would otherwise all start on bank 0); V keeps 64-byte group g of
+// row r at g ^ (r & 3) (d >= 128) or g ^ ((r >> 1) & 1) (d = 64), so the 4
+// rows one pass of a transposing read covers do. Both swizzles depend on the lane only through lane / 16, the
+// wave and (K at d = 256) whether the DMA instruction is the odd one of its
+// pair, so each wave's DMA instructions of a tile part need at most two
+// per-lane source offsets.
 template <typename E, int D, bool CAUSAL>
 __global__ __launch_bounds__(512, 1) void attn_fwd_pp_kernel(
     const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict__ V, E* __restrict__ O,
     float* __restrict__ LSE, int BH, int Nq, int Nk, int nq, float c) {
-  static_assert(D == 64 || D == 128, "the ping-pong kernel is laid out for d = 64 and 128");
-  constexpr int QB = 2, NW = 8, NST = 3;
-  constexpr int BN = D == 128 ? 32 : 64;      // keys per tile: 8 KiB of K, 8 of V
+  static_assert(D == 64 || D == 128 || D == 256, "the ping-pong kernel: d = 64, 128, 256");
+  constexpr int QB = D == 256 ? 1 : 2, NW = 8, NST = 3;
+  constexpr int BN = D == 64 ? 64 : 32;       // keys per tile: 8 KiB of K, 8 of V (16 at d = 256)
   constexpr int NKB = BN / 32;                // 32-key blocks per tile
   constexpr int NDB = D / 32;                 // 32-column blocks of O
   constexpr uint32_t ROWB = D * 2;            // bytes per row
@@ -612,12 +618,15 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_pp_kernel(
   constexpr int HALF = 4 * RPI;               // rows per 4-wave DMA round
   constexpr uint32_t TB = BN * ROWB;          // bytes per K or V tile
   constexpr uint32_t SB = 2 * TB;             // bytes per stage
-  static_assert(TB == 8192 && 2 * HALF == BN, "two DMA instructions a wave per tile part");
+  constexpr int NI = TB / 4096;               // DMA instructions a wave per tile part
+  static_assert(TB % 8192 == 0 && NI * HALF == BN, "whole DMA rounds per tile part");
+  constexpr int NPV = 2 * NDB * NKB;          // P*V MFMAs (operand fragments) per tile
+  constexpr int NSG = D / 16 * NKB;           // S MFMAs (operand fragments) per tile
   // Swizzles: K chunk c of row r sits at c ^ kswz(r), V 64-byte group g at
   // g ^ vswz(r); within one wave's DMA instructions both depend on r only
-  // through lane / 16.
-  auto kswz = [](int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); };
-  auto vswz = [](int r) { return D == 128 ? (r & 3) : ((r >> 1) & 1); };
+  // through lane / 16 and (K at d = 256) whether the instruction is even.
+  auto kswz = [](int r) { return D >= 128 ? (r & 15) : ((r >> 1) & 7); };
+  auto vswz = [](int r) { return D >= 128 ? (r & 3) : ((r >> 1) & 1); };
   typedef typename Elem<E>::v8 v8;
   typedef typename Elem<E>::v4 v4;
   __shared__ __attribute__((aligned(1024))) char smem[NST * SB];
@@ -673,30 +682,32 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_pp_kernel(
   const char* const lds = smem;
   lds_char* const lds3 = to_lds(smem);
 
-  // DMA source offset of this lane (row 4 w' + lane / 16 of a 16-row half,
-  // the logical chunk its physical slot lane % 16 holds): K for the late
-  // waves, V for the early ones.
-  uint32_t dsrc;
-  {
-    const int r = RPI * dwave + lane / CPR, pc = lane % CPR;
+  // DMA source offsets of this lane (row RPI w' + lane / CPR of a DMA
+  // round's HALF rows, the logical chunk its physical slot lane % CPR holds)
+  // for even and odd instructions: K for the late waves, V for the early
+  // ones. The two differ only for K at d = 256.
+  uint32_t dsrc[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int rl = RPI * dwave + lane / CPR, pc = lane % CPR, r = rl + HALF * e;
     const int ck = pc ^ kswz(r);
     const int cv = 4 * ((pc >> 2) ^ vswz(r)) + (pc & 3);
-    dsrc = (uint32_t)(r * (int)ROWB + 16 * (late ? ck : cv));
+    dsrc[e] = (uint32_t)(rl * (int)ROWB + 16 * (late ? ck : cv));
   }
-  // This wave's two DMA instructions of the K (late waves) or V (early
+  // This wave's NI DMA instructions of the K (late waves) or V (early
   // waves) part of the tile from key k0, into the stage at byte `base`. Each
-  // 16-row half goes through a resource based at its first row whose record
-  // count ends at the head's last key (zero if the half lies past it), so
+  // round of HALF rows goes through a resource based at its first row whose
+  // record count ends at the head's last key (zero if it lies past it), so
   // rows past Nk come back as zeros.
   auto dma = [&](uint32_t base, int k0) __attribute__((always_inline)) {
     const E* src = late ? K : V;
     const uint32_t part = late ? 0u : TB;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < NI; ++i) {
       const int r0 = k0 + HALF * i;
       const uint32_t n = r0 < Nk ? (uint32_t)(Nk - r0) * ROWB : 0u;
       load16_lds(make_rsrc(src + khead + (size_t)r0 * D, n),
-                 lds3 + base + part + 1024 * (dwave + 4 * i), dsrc);
+                 lds3 + base + part + 1024 * (dwave + 4 * i), dsrc[i & 1]);
     }
   };
   // Read bases: K fragment j of lane (col, half) is logical chunk 2 j + half
@@ -845,13 +856,13 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_pp_kernel(
   auto pv = [&](uint32_t base, auto tail) __attribute__((always_inline)) {
     v8 f[4] = {vpre[0], vpre[1], vpre[2], v8{}};
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      if (i + 3 < 8) f[(i + 3) % 4] = vfrag(base, i + 3);
+    for (int i = 0; i < NPV; ++i) {
+      if (i + 3 < NPV) f[(i + 3) % 4] = vfrag(base, i + 3);
       const v8 a = f[i % 4];
       const int kbk = i / (2 * NDB), sg = (i / NDB) % 2, db = i % NDB;
 #pragma unroll
       for (int b = 0; b < QB; ++b) oacc[b][db] = Elem<E>::mfma(a, pb[b][kbk][sg], oacc[b][db]);
-      if (i == 5) tail();
+      if (i == NPV - 3) tail();
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -861,8 +872,8 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_pp_kernel(
   auto sgemm = [&](f32x16 (&sacc)[QB][NKB], uint32_t base, v8 (&g)[4], auto after0)
       __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (j + 3 < 8) g[(j + 3) % 4] = kfrag(base, j + 3);
+    for (int j = 0; j < NSG; ++j) {
+      if (j + 3 < NSG) g[(j + 3) % 4] = kfrag(base, j + 3);
       const v8 a = g[j % 4];
       const int kbk = j / (D / 16), jj = j % (D / 16);
 #pragma unroll
@@ -901,15 +912,6 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_pp_kernel(
 #pragma unroll
       for (int j = 0; j < 3; ++j) g[j] = kfrag(bcur, j);
     };
-    // P*V of tile t-1 runs for every wave: one that skipped that tile holds
-    // zero weights and adds exact zeros (its V rows are real data, or zeros
-    // past the end). The first tile has no predecessor.
-    if constexpr (first) {
-      kread();
-    } else {
-      pv(bprev, kread);
-    }
-    __builtin_amdgcn_sched_barrier(0);
     // The early waves load V of tile t+1 into the next stage, the late ones K
     // of tile t+2 into the previous one; issued without a branch (a tile past
     // the last one is loaded as zeros into a stage nobody reads again), after
@@ -918,10 +920,48 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_pp_kernel(
       dma(late ? bprev : bnext, (t + (late ? 2 : 1)) * BN);
     };
     f32x16 sacc[QB][NKB];
-    if (do_s) {
-      sgemm(sacc, bcur, g, issue_dma);
+    if constexpr (D == 256 && !first) {
+      // One query block: the P*V MFMAs of tile t-1 and the S MFMAs of tile t
+      // alternate, so that the chain of 16 dependent S MFMAs has an
+      // independent MFMA between each two of its steps. Operands 0-2 (V^T 0,
+      // K 0, V^T 1) were read at the end of the softmax phase before. A wave
+      // past its rows computes S anyway (the MFMA stream has no branch) and
+      // drops it.
+      v8 f[4] = {vpre[0], vpre[1], vpre[2], v8{}};
+#pragma unroll
+      for (int m = 0; m < 2 * NPV; ++m) {
+        const int u = m + 3;
+        if (u < 2 * NPV) f[u % 4] = (u & 1) ? kfrag(bcur, u / 2) : vfrag(bprev, u / 2);
+        const v8 a = f[m % 4];
+        if (m & 1) {
+          const int j = m / 2;
+          sacc[0][0] = j == 0 ? Elem<E>::mfma(a, qf[0][0], f32x16{})
+                              : Elem<E>::mfma(a, qf[0][j], sacc[0][0]);
+        } else {
+          const int i = m / 2, sg = (i / NDB) % 2, db = i % NDB;
+          oacc[0][db] = Elem<E>::mfma(a, pb[0][0][sg], oacc[0][db]);
+        }
+        if (m == 1) {
+          __builtin_amdgcn_sched_barrier(0);
+          issue_dma();
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
     } else {
-      issue_dma();
+      // P*V of tile t-1 runs for every wave: one that skipped that tile holds
+      // zero weights and adds exact zeros (its V rows are real data, or zeros
+      // past the end). The first tile has no predecessor.
+      if constexpr (first) {
+        kread();
+      } else {
+        pv(bprev, kread);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (do_s) {
+        sgemm(sacc, bcur, g, issue_dma);
+      } else {
+        issue_dma();
+      }
     }
     __builtin_amdgcn_s_setprio(0);
     barrier();
@@ -935,8 +975,16 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_pp_kernel(
     }
     __builtin_amdgcn_sched_barrier(0);
     refresh();
+    if constexpr (D == 256) {
+      // K of tile t+1 was loaded in M(t-1) and waited for by the end of the
+      // late waves' X(t-1).
+      vpre[0] = vfrag(bcur, 0);
+      vpre[1] = kfrag(bnext, 0);
+      vpre[2] = vfrag(bcur, 1);
+    } else {
 #pragma unroll
-    for (int i = 0; i < 3; ++i) vpre[i] = vfrag(bcur, i);
+      for (int i = 0; i < 3; ++i) vpre[i] = vfrag(bcur, i);
+    }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's DMA
     barrier();
   };
@@ -960,8 +1008,13 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_pp_kernel(
   // P*V of the last tile; the early waves then wait at the barrier that
   // evens the counts.
   if (nt >= 1 && nt - 1 < wave_nt) {
+    const uint32_t blast = ((nt - 1) % NST) * SB;
+    if constexpr (D == 256) {  // vpre holds V^T 0, K 0, V^T 1
+      vpre[1] = vpre[2];
+      vpre[2] = vfrag(blast, 2);
+    }
     __builtin_amdgcn_s_setprio(1);
-    pv(((nt - 1) % NST) * SB, []() {});
+    pv(blast, []() {});
     __builtin_amdgcn_s_setprio(0);
   }
   if (!late) barrier();
@@ -1006,7 +1059,8 @@ void tile_info(Shape* sh) {
 }
 
 constexpr int64_t kCUs = 256;  // gfx950 parts have 256 CUs
-// LDS of the ping-pong kernel: three stages of 8 KiB of K and 8 KiB of V.
+// LDS of the ping-pong kernel: three stages of 8 KiB of K and 8 KiB of V
+// (of 16 KiB each at d = 256).
 constexpr int kPingPongLds = 3 * 2 * 8192;
 
 // The workgroup shape at d = 128: the largest whose grid still gives every CU
@@ -1062,6 +1116,7 @@ int check_sizes(int B, int H, int Nq, int Nk, int d, Shape* sh) {
   sh->block = 64 * sh->nw;
   sh->block_m = 32 * sh->nw * sh->qb;
   if ((d == 64 || d == 128) && sh->qb == 2 && sh->nw == 8) sh->lds = kPingPongLds;
+  if (d == 256 && sh->nw == 8) sh->lds = 2 * kPingPongLds;
   const int64_t nq = ((int64_t)Nq + sh->block_m - 1) / sh->block_m;
   const int64_t grid = (int64_t)B * H * nq;
   if (grid > INT32_MAX) return ATTN_ERR_SHAPE;
@@ -1115,7 +1170,10 @@ hipError_t launch(const Shape& sh, const Args& a) {
 
 template <typename E, int D, bool CAUSAL>
 hipError_t launch_shape(const Shape& sh, const Args& a) {
-  if constexpr (D == 32 || D == 96 || D == 256) {
+  if constexpr (D == 256) {
+    if (sh.nw == 8) return launch_pp<E, D, CAUSAL>(sh, a);
+  }
+  if constexpr (D == 32 || D == 96) {
     if (sh.nw == 8) return launch<E, D, CAUSAL, 1, 8>(sh, a);
   }
   if constexpr (D == 64 || D == 128) {
