@@ -192,7 +192,7 @@ const char* attn_strerror(int status);
  * without launching: workgroups in the 1-D grid, threads per workgroup, LDS
  * bytes per workgroup, query rows per workgroup (block_m) and keys per inner
  * step (block_n). The workgroup shape depends on the grid: bigger
- * workgroups (256 query rows in 512 threads, or at d = 64 and 128 512 rows)
+ * workgroups (256 query rows in 512 threads, or at d = 64, 96 and 128 512 rows)
  * when B, H and N still give every CU enough of them (at d = 64 also only
  * when N >= 4096). Out-params may
  * not be NULL. Returns the same validation

@@ -378,14 +378,28 @@ def test_launch_shape_d64_follows_the_grid_and_the_rows(lib, B, H, N, rows):
 @pytest.mark.parametrize("B,H,N,rows", [(16, 16, 4096, 256), (1, 32, 16384, 256),
                                         (4, 16, 4000, 256), (2, 16, 4000, 128),
                                         (4, 16, 1024, 128)])
+def test_launch_shape_d32_follows_the_grid(lib, B, H, N, rows):
+    # d = 32 takes eight-wave, 256-row workgroups when the grid gives two full
+    # rounds of two per CU, else four-wave, 128-row ones
+    s = mi.attn_fwd_launch_shape(B, H, N, 32, True)
+    assert s["block_m"] == rows
+    assert s["block"] == (512 if rows == 256 else 256)
+    assert s["grid"] == B * H * ((N + rows - 1) // rows)
+
+
+@pytest.mark.parametrize("B,H,N,rows", [(16, 16, 4096, 512), (1, 32, 16384, 512),
+                                        (4, 16, 4000, 512), (2, 16, 4000, 128),
+                                        (4, 16, 1024, 128)])
 def test_launch_shape_d96_follows_the_grid(lib, B, H, N, rows):
-    # d = 96 (and d = 32) take eight-wave, 256-row workgroups when the grid
-    # gives two full rounds of two per CU, else four-wave, 128-row ones
-    for d in (96, 32):
-        s = mi.attn_fwd_launch_shape(B, H, N, d, True)
-        assert s["block_m"] == rows
-        assert s["block"] == (512 if rows == 256 else 256)
-        assert s["grid"] == B * H * ((N + rows - 1) // rows)
+    # d = 96 takes the ping-pong kernel's 512-row workgroups (two blocks a
+    # wave, eight waves, 48 KiB of LDS) when the grid gives every CU two of
+    # them, else four-wave, 128-row ones
+    s = mi.attn_fwd_launch_shape(B, H, N, 96, True)
+    assert s["block_m"] == rows
+    assert s["block"] == (512 if rows == 512 else 256)
+    assert s["grid"] == B * H * ((N + rows - 1) // rows)
+    if rows == 512:
+        assert s["lds_bytes"] == 3 * 2 * 8192
 
 
 @pytest.mark.parametrize("B,H,N,rows", [(16, 16, 4096, 256), (1, 32, 16384, 256),
@@ -397,3 +411,5 @@ def test_launch_shape_d256_follows_the_grid(lib, B, H, N, rows):
     assert s["block_m"] == rows
     assert s["block"] == (512 if rows == 256 else 256)
     assert s["grid"] == B * H * ((N + rows - 1) // rows)
+    if rows == 256:  # the ping-pong kernel: three stages of 16 KiB of K and 16 of V
+        assert s["lds_bytes"] == 3 * 2 * 16384

@@ -477,11 +477,12 @@ def test_ex_long_sampled(d, N, causal, dt):
 # d = 128 picks its workgroup shape from the grid size: 512 query rows a
 # workgroup (two blocks of 32 a wave, eight waves) when the grid still gives
 # each CU two workgroups' worth, else 256 (two blocks, four waves), else 128
-# (one block, four waves). d = 96 takes eight one-block waves (256 rows) on
-# grids of two full rounds, else four. Each case below lands on one shape,
-# with ragged lengths and (causal) Nq != Nk, checked on sampled rows of a few
-# heads. d = 256 takes eight one-block waves on grids of two full rounds
-# of one workgroup per CU, d = 32 as d = 96.
+# (one block, four waves). d = 96 takes the 512-row shape (the ping-pong
+# kernel) when the grid gives every CU two workgroups, else 128 rows. Each
+# case below lands on one shape, with ragged lengths and (causal) Nq != Nk,
+# checked on sampled rows of a few heads. d = 256 takes eight one-block waves
+# on grids of two full rounds of one workgroup per CU, d = 32 on grids of two
+# full rounds of two per CU, else four.
 SHAPES = [
     # (d, B, H, Nq, Nk, causal, rows per workgroup, element type)
     (128, 8, 16, 4000, 4000, False, 512, "bf16"),
@@ -496,10 +497,10 @@ SHAPES = [
     (64, 4, 16, 4100, 4100, True, 512, "f16"),
     (64, 5, 16, 4096, 6000, True, 512, "bf16"),
     (64, 4, 16, 4000, 4000, True, 128, "bf16"),
-    (96, 4, 16, 4000, 4000, False, 256, "bf16"),
-    (96, 4, 16, 4000, 4000, True, 256, "bf16"),
-    (96, 6, 16, 3000, 4100, True, 256, "bf16"),
-    (96, 4, 16, 4000, 4000, False, 256, "f16"),
+    (96, 4, 16, 4000, 4000, False, 512, "bf16"),
+    (96, 4, 16, 4000, 4000, True, 512, "bf16"),
+    (96, 6, 16, 3000, 4100, True, 512, "bf16"),
+    (96, 4, 16, 4000, 4000, False, 512, "f16"),
     (96, 2, 16, 4000, 4000, True, 128, "bf16"),
     (256, 2, 16, 4000, 4000, False, 256, "bf16"),
     (256, 3, 16, 3000, 4100, True, 256, "f16"),
@@ -536,7 +537,7 @@ def test_workgroup_shapes(d, B, H, Nq, Nk, causal, rows, dt):
                               f"head ({b},{h})")
 
 
-@pytest.mark.parametrize("d,rows", [(128, 512), (256, 256), (96, 256), (64, 512)])
+@pytest.mark.parametrize("d,rows", [(128, 512), (256, 256), (96, 512), (64, 512)])
 @pytest.mark.parametrize("times", [-1.0, 0.0, 2.0])
 @pytest.mark.parametrize("causal", [False, True])
 def test_scales_on_the_eight_wave_shapes(d, rows, times, causal):

@@ -110,18 +110,19 @@ constexpr bool kVDma = D == 64 || D == 96 || D == 128 || D == 256;
 // d = 256, and with the bit-select mask below +1.4% on causal d = 64.
 
 // Workgroup shapes: QB 32-query blocks per wave, NW waves per workgroup (the
-// 512-row shape at d = 128, QB = 2 and NW = 8, and the 256-row shape at
-// d = 256 run the ping-pong kernel).
-// d = 32, 96 and 256 have two, chosen at launch by the size of the grid:
-// eight waves of one block (256 rows) on big grids, which halves the
-// HBM -> LDS staging per FLOP, else four waves. At d = 96 (two workgroups
-// per CU, four waves per SIMD) that gave +2.7% on B=16 H=16 N=4096 and +3.4%
-// on the long causal shape, at d = 256 (one per CU, two waves per SIMD)
-// +3.9% and +6.7%, at d = 32 (two per CU) +3.5% and +2.3% (interleaved
-// A/Bs). At d = 256 the ping-pong kernel then ran those eight waves 1.9% and
-// 2.7% faster than this kernel. At d = 64 eight waves gained +0.5% on big grids and
-// lost 2.6-2.8% on the two small workloads, so d = 64 keeps four. d = 128
-// has three:
+// 512-row shape at d = 64, 96 and 128, QB = 2 and NW = 8, and the 256-row
+// shape at d = 256 run the ping-pong kernel).
+// d = 32 and 256 have two, chosen at launch by the size of the grid: eight
+// waves of one block (256 rows) on big grids, which halves the HBM -> LDS
+// staging per FLOP, else four waves. At d = 256 (one per CU, two waves per
+// SIMD) that gave +3.9% and +6.7% on B=16 H=16 N=4096 and the long causal
+// shape, at d = 32 (two per CU) +3.5% and +2.3% (interleaved A/Bs); at d = 96
+// (two per CU, four waves per SIMD) +2.7% and +3.4%, before the ping-pong
+// kernel's 512 rows replaced it there (a further +2.9% to +8.5% on four
+// shapes). At d = 256 the ping-pong kernel then ran those eight waves 1.9%
+// and 2.7% faster than this kernel. At d = 64 eight waves gained +0.5% on big
+// grids and lost 2.6-2.8% on the two small workloads, so d = 64 keeps four
+// outside the ping-pong kernel's long rows. d = 128 has three:
 // - QB = 2, NW = 8 (512 rows a workgroup, one per CU, two waves per SIMD),
 //   in the ping-pong kernel: +8.9% on B=16 H=16 N=4096 and +9.5% on the long
 //   causal shape over the same shape run by this kernel, whose two waves of a
@@ -136,14 +137,15 @@ constexpr bool kVDma = D == 64 || D == 96 || D == 128 || D == 256;
 // and by 2.2% on the long causal shape. Eight waves a workgroup then halve
 // the HBM -> LDS staging per FLOP again: a further +2.0% and +0.9% (all
 // interleaved A/Bs, bit-identical outputs). Bigger workgroups mean fewer of
-// them, so small grids keep the smaller shapes. At d = 96 (-1.1%, -6%) and
-// d = 64 (-12% on the two small workloads) two blocks lost to the fourth
-// one-block wave per SIMD, so every other d runs QB = 1, NW = 4.
+// them, so small grids keep the smaller shapes. In this kernel two blocks a
+// wave lost to the fourth one-block wave per SIMD at d = 96 (-1.1%, -6%) and
+// d = 64 (-12% on the two small workloads), so below the ping-pong kernel's
+// shapes every other d runs QB = 1, NW = 4.
 // Workgroups per CU the register allocation must allow.
 template <int D, int QB, int NW>
 constexpr int kMinBlocks =
     QB == 2 ? 8 / NW
-    : NW == 8 ? (D == 256 ? 1 : 2)  // eight-wave shapes: d = 32, 96 two a CU, d = 256 one
+    : NW == 8 ? (D == 256 ? 1 : 2)  // eight-wave shapes: d = 32 two a CU, d = 256 one
               : (D == 64 ? 4 : D == 96 || D == 128 ? 3 : 2);
 // The most query rows a workgroup has (the 32-bit offset check on Nq allows
 // for one workgroup's rows past the end).
@@ -577,7 +579,7 @@ __global__ __launch_bounds__(64 * NW, (kMinBlocks<D, QB, NW>)) void attn_fwd_ker
   }
 }
 
-// ------------------------------ ping-pong kernel (d = 64, 128 and 256, big grids) --
+// ----------------------------- ping-pong kernel (d = 64, 96, 128, 256, big grids) --
 // 512 query rows a workgroup of 8 waves, two 32-query blocks a wave (256 rows,
 // one block a wave, at d = 256); waves w and w + 4 share a SIMD. Each wave
 // alternates an MFMA phase M(t) (O^T += V^T P^T of tile t-1, then
@@ -593,26 +595,31 @@ __global__ __launch_bounds__(64 * NW, (kMinBlocks<D, QB, NW>)) void attn_fwd_ker
 // with the P*V MFMAs.
 //
 // Tiles of 8 KiB of K and 8 of V (32 keys at d = 128, 64 at d = 64; 16 KiB
-// each of 32 keys at d = 256), rows without padding, in a ring of three LDS
-// stages (K at +0, V after it). K keeps 16-byte chunk c of row r at chunk
-// c ^ (r & 15) (d >= 128) or c ^ ((r >> 1) & 7) (d = 64), so the 16 rows one
-// pass of a 16-byte read covers hit all 64 banks (rows 256 or 512 bytes
-// apart would otherwise all start on bank 0); V keeps 64-byte group g of
-// row r at g ^ (r & 3) (d >= 128) or g ^ ((r >> 1) & 1) (d = 64), so the 4
-// rows one pass of a transposing read covers do. Both swizzles depend on the lane only through lane / 16, the
-// wave and (K at d = 256) whether the DMA instruction is the odd one of its
-// pair, so each wave's DMA instructions of a tile part need at most two
-// per-lane source offsets.
+// each of 32 keys at d = 256; at d = 96 32 keys laid out as at d = 128, whose
+// chunks 12-15 of each row the DMA fills with zeros and no read touches),
+// rows without padding, in a ring of three LDS stages (K at +0, V after it).
+// K keeps 16-byte chunk c of row r at chunk c ^ (r & 15) (d >= 96) or
+// c ^ ((r >> 1) & 7) (d = 64), so the 16 rows one pass of a 16-byte read
+// covers hit all 64 banks (rows 256 or 512 bytes apart would otherwise all
+// start on bank 0); V keeps 64-byte group g of row r at g ^ (r & 3)
+// (d >= 96) or g ^ ((r >> 1) & 1) (d = 64), so the 4 rows one pass of a
+// transposing read covers do. Both swizzles depend on the lane only through
+// lane / 16, the wave and (K at d = 256) whether the DMA instruction is the
+// odd one of its pair, so each wave's DMA instructions of a tile part need
+// at most two per-lane source offsets.
 template <typename E, int D, bool CAUSAL>
 __global__ __launch_bounds__(512, 1) void attn_fwd_pp_kernel(
     const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict__ V, E* __restrict__ O,
     float* __restrict__ LSE, int BH, int Nq, int Nk, int nq, float c) {
-  static_assert(D == 64 || D == 128 || D == 256, "the ping-pong kernel: d = 64, 128, 256");
+  static_assert(D == 64 || D == 96 || D == 128 || D == 256,
+                "the ping-pong kernel: d = 64, 96, 128, 256");
   constexpr int QB = D == 256 ? 1 : 2, NW = 8, NST = 3;
   constexpr int BN = D == 64 ? 64 : 32;       // keys per tile: 8 KiB of K, 8 of V (16 at d = 256)
   constexpr int NKB = BN / 32;                // 32-key blocks per tile
   constexpr int NDB = D / 32;                 // 32-column blocks of O
-  constexpr uint32_t ROWB = D * 2;            // bytes per row
+  constexpr int DL = D == 96 ? 128 : D;       // row width in LDS (d = 96: chunks 12-15 zero)
+  constexpr uint32_t ROWB = DL * 2;           // bytes per row in LDS
+  constexpr uint32_t GROWB = D * 2;           // bytes per row in HBM
   constexpr int CPR = ROWB / 16;              // 16-byte chunks per row
   constexpr int RPI = 1024 / ROWB;            // rows per DMA instruction
   constexpr int HALF = 4 * RPI;               // rows per 4-wave DMA round
@@ -625,8 +632,8 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_pp_kernel(
   // Swizzles: K chunk c of row r sits at c ^ kswz(r), V 64-byte group g at
   // g ^ vswz(r); within one wave's DMA instructions both depend on r only
   // through lane / 16 and (K at d = 256) whether the instruction is even.
-  auto kswz = [](int r) { return D >= 128 ? (r & 15) : ((r >> 1) & 7); };
-  auto vswz = [](int r) { return D >= 128 ? (r & 3) : ((r >> 1) & 1); };
+  auto kswz = [](int r) { return DL >= 128 ? (r & 15) : ((r >> 1) & 7); };
+  auto vswz = [](int r) { return DL >= 128 ? (r & 3) : ((r >> 1) & 1); };
   typedef typename Elem<E>::v8 v8;
   typedef typename Elem<E>::v4 v4;
   __shared__ __attribute__((aligned(1024))) char smem[NST * SB];
@@ -685,14 +692,17 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_pp_kernel(
   // DMA source offsets of this lane (row RPI w' + lane / CPR of a DMA
   // round's HALF rows, the logical chunk its physical slot lane % CPR holds)
   // for even and odd instructions: K for the late waves, V for the early
-  // ones. The two differ only for K at d = 256.
+  // ones. The two differ only for K at d = 256. At d = 96 a slot whose
+  // logical chunk lies past the row's 12 gets an offset past any buffer:
+  // zeros, no fetch.
   uint32_t dsrc[2];
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
     const int rl = RPI * dwave + lane / CPR, pc = lane % CPR, r = rl + HALF * e;
     const int ck = pc ^ kswz(r);
     const int cv = 4 * ((pc >> 2) ^ vswz(r)) + (pc & 3);
-    dsrc[e] = (uint32_t)(rl * (int)ROWB + 16 * (late ? ck : cv));
+    const int lc = late ? ck : cv;
+    dsrc[e] = lc < D / 8 ? (uint32_t)(rl * (int)GROWB + 16 * lc) : 0x80000000u;
   }
   // This wave's NI DMA instructions of the K (late waves) or V (early
   // waves) part of the tile from key k0, into the stage at byte `base`. Each
@@ -705,7 +715,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_pp_kernel(
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int r0 = k0 + HALF * i;
-      const uint32_t n = r0 < Nk ? (uint32_t)(Nk - r0) * ROWB : 0u;
+      const uint32_t n = r0 < Nk ? (uint32_t)(Nk - r0) * GROWB : 0u;
       load16_lds(make_rsrc(src + khead + (size_t)r0 * D, n),
                  lds3 + base + part + 1024 * (dwave + 4 * i), dsrc[i & 1]);
     }
@@ -779,17 +789,18 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_pp_kernel(
       }
     }
     // Each block's row sum runs in four chains (weights i = 0, 1, 2, 3 mod 4),
-    // added at the end, rather than one serial chain. At d = 64 one test also
-    // covers both blocks' rebase, so that the compiler interleaves the two
-    // blocks' weights instead of finishing one block before the other's
-    // branch; at d = 128 that keeps too many values live across the branch
-    // and spills, so each block keeps its own test there. Measured
+    // added at the end, rather than one serial chain. At d = 64 and 96 one
+    // test also covers both blocks' rebase, so that the compiler interleaves
+    // the two blocks' weights instead of finishing one block before the
+    // other's branch; at d = 128 that keeps too many values live across the
+    // branch and spills, so each block keeps its own test there. Measured
     // interleaved: +0.7% at d = 64 (B=16 H=16 N=4096 and the long causal
-    // shape), +0.3% and +0.4% on the two d = 128 workloads. This phase runs
+    // shape), +0.3% and +0.4% on the two d = 128 workloads; the joint test
+    // added +0.4% to +0.7% on four d = 96 shapes. This phase runs
     // on one wave of the SIMD, and one wave issues at most one VALU
     // instruction every ~9 cycles whatever the dependences (measured), so
     // its length is set by its instruction count.
-    constexpr bool kJointRebase = D == 64;
+    constexpr bool kJointRebase = D == 64 || D == 96;
     float tsum[QB], part[QB][4];
     auto weight = [&](int b, int kb, int i) __attribute__((always_inline)) {
       const float p = __builtin_amdgcn_exp2f(fmaf(sacc[b][kb][i], c, -m_run[b]));
@@ -1086,9 +1097,15 @@ void pick_shape_64(int64_t BH, int Nq, int Nk, int* qb, int* nw) {
   if (Nq >= 4096 && Nk >= 4096 && BH * (((int64_t)Nq + 511) / 512) >= 2 * kCUs) *qb = 2, *nw = 8;
 }
 
-// d = 32, 96 and 256 (one block a wave): eight-wave workgroups (256 rows)
-// when the grid gives two full rounds of them (two per CU at d = 32 and 96,
-// one at d = 256), else four waves.
+// d = 96: the ping-pong kernel's 512-row workgroups when the grid gives every
+// CU two of them, else one block a wave.
+void pick_shape_96(int64_t BH, int Nq, int* qb, int* nw) {
+  if (BH * (((int64_t)Nq + 511) / 512) >= 2 * kCUs) *qb = 2, *nw = 8;
+}
+
+// d = 32 and 256 (one block a wave): eight-wave workgroups (256 rows) when
+// the grid gives two full rounds of them (two per CU at d = 32, one at
+// d = 256), else four waves.
 int pick_waves_one_block(int64_t BH, int Nq, int d) {
   const int64_t per_round = (d == 256 ? 1 : 2) * kCUs;
   return BH * (((int64_t)Nq + 255) / 256) >= 2 * per_round ? 8 : 4;
@@ -1112,10 +1129,11 @@ int check_sizes(int B, int H, int Nq, int Nk, int d, Shape* sh) {
   sh->qb = 1, sh->nw = kWaves;
   if (d == 128) pick_shape_128((int64_t)B * H, Nq, &sh->qb, &sh->nw);
   if (d == 64) pick_shape_64((int64_t)B * H, Nq, Nk, &sh->qb, &sh->nw);
-  if (d == 32 || d == 96 || d == 256) sh->nw = pick_waves_one_block((int64_t)B * H, Nq, d);
+  if (d == 32 || d == 256) sh->nw = pick_waves_one_block((int64_t)B * H, Nq, d);
+  if (d == 96) pick_shape_96((int64_t)B * H, Nq, &sh->qb, &sh->nw);
   sh->block = 64 * sh->nw;
   sh->block_m = 32 * sh->nw * sh->qb;
-  if ((d == 64 || d == 128) && sh->qb == 2 && sh->nw == 8) sh->lds = kPingPongLds;
+  if ((d == 64 || d == 96 || d == 128) && sh->qb == 2 && sh->nw == 8) sh->lds = kPingPongLds;
   if (d == 256 && sh->nw == 8) sh->lds = 2 * kPingPongLds;
   const int64_t nq = ((int64_t)Nq + sh->block_m - 1) / sh->block_m;
   const int64_t grid = (int64_t)B * H * nq;
@@ -1173,7 +1191,10 @@ hipError_t launch_shape(const Shape& sh, const Args& a) {
   if constexpr (D == 256) {
     if (sh.nw == 8) return launch_pp<E, D, CAUSAL>(sh, a);
   }
-  if constexpr (D == 32 || D == 96) {
+  if constexpr (D == 96) {
+    if (sh.qb == 2 && sh.nw == 8) return launch_pp<E, D, CAUSAL>(sh, a);
+  }
+  if constexpr (D == 32) {
     if (sh.nw == 8) return launch<E, D, CAUSAL, 1, 8>(sh, a);
   }
   if constexpr (D == 64 || D == 128) {
