@@ -508,6 +508,12 @@ SHAPES = [
     (32, 4, 16, 4000, 4000, True, 256, "bf16"),
     (32, 6, 16, 3000, 4100, False, 256, "f16"),
     (32, 2, 16, 4000, 4000, False, 128, "bf16"),
+    # the ping-pong shapes with causal Nk < Nq: the first Nq - Nk rows see no
+    # key (o = 0, lse = -inf), whole waves and workgroups among them
+    (128, 8, 16, 4000, 1500, True, 512, "bf16"),
+    (96, 8, 16, 4000, 1500, True, 512, "f16"),
+    (64, 4, 16, 6000, 4100, True, 512, "bf16"),
+    (256, 16, 16, 600, 300, True, 256, "bf16"),
 ]
 
 
