@@ -13,10 +13,11 @@
 // two blocks of 32 that share every K and V fragment it reads from LDS. Two
 // (d=128), three (d=96) or four (d=64) workgroups share a CU, so each SIMD
 // holds waves of different workgroups whose softmax (VALU) and matrix (MFMA)
-// phases interleave. On big grids at d = 128 a separate kernel (further down)
-// runs 512-row workgroups whose two wave groups alternate the two kinds of
-// work by barrier, a phase apart. Keys and values
-// stream through LDS in tiles of 32 (d=128) or 64 (d=64) keys, double
+// phases interleave. On big grids (d = 96 and 128, d = 64 on long rows:
+// 512-row workgroups; d = 256: 256 rows) a separate kernel (further down)
+// runs eight waves whose two groups alternate the two kinds of work by
+// barrier, a phase apart; d = 32 runs eight one-block waves there. Keys and
+// values stream through LDS in tiles of 32 (d=128) or 64 (d=64) keys, double
 // buffered one tile ahead with one barrier per tile: at d = 64, 96, 128 and
 // 256 both, by buffer loads that write LDS directly (LDS DMA),
 // each tile through a buffer resource based at its first row; the rest
@@ -145,7 +146,7 @@ constexpr bool kVDma = D == 64 || D == 96 || D == 128 || D == 256;
 template <int D, int QB, int NW>
 constexpr int kMinBlocks =
     QB == 2 ? 8 / NW
-    : NW == 8 ? (D == 256 ? 1 : 2)  // eight-wave shapes: d = 32 two a CU, d = 256 one
+    : NW == 8 ? (D == 256 ? 1 : 2)  // eight waves (d = 32 only): two a CU
               : (D == 64 ? 4 : D == 96 || D == 128 ? 3 : 2);
 // The most query rows a workgroup has (the 32-bit offset check on Nq allows
 // for one workgroup's rows past the end).
