@@ -626,3 +626,54 @@ def test_large_scale_rounding_bound(d, times, causal, all_heads):
         worst_l = max(worst_l, el)
     print(f"  max|dO|={worst_err:.3e} (largest share of the bound {worst_ratio:.3f}) "
           f"max|dlse|={worst_l:.3e}", flush=True)
+
+
+# ------------------------------------------------- seeded random shapes --
+
+def _random_shape_cases(n=40, seed=20261203, cap=1 << 25):
+    """Shapes drawn at random with a fixed seed, across every head dim, both
+    element types, with and without the mask, self and cross lengths (half
+    log-uniform from 1, half from 2000 to 6000). Sizes go up to
+    B*H*max(Nq, Nk)*d = cap (half the cases at the cap), so that about half
+    land on the big-grid workgroup shapes and the rest on the small ones."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        d = int(rng.choice([32, 64, 64, 96, 128, 128, 256]))
+        dt = "bf16" if rng.random() < 0.6 else "f16"
+        causal = bool(rng.random() < 0.5)
+        length = lambda: int(np.exp(rng.uniform(0.0, np.log(6000.0))) if rng.random() < 0.5
+                             else rng.integers(2000, 6001))
+        nq = length()
+        nk = nq if rng.random() < 0.6 else length()
+        bh_max = max(1, cap // (max(nq, nk) * d))
+        bh = bh_max if rng.random() < 0.5 else int(np.exp(rng.uniform(0.0, np.log(bh_max))))
+        H = max(h for h in (1, 2, 4, 8, 16) if h <= bh)
+        B = max(1, bh // H)
+        cases.append((d, B, H, nq, nk, causal, dt))
+    return cases
+
+
+@pytest.mark.parametrize("d,B,H,Nq,Nk,causal,dt", _random_shape_cases())
+def test_random_shapes(d, B, H, Nq, Nk, causal, dt):
+    rows_per_wg = mi.attn_fwd_launch_shape(B, H, Nq, d, causal)["block_m"]
+    announce(f"random shape d={d} B={B} H={H} Nq={Nq} Nk={Nk} causal={causal} {dt} "
+             f"rows/workgroup={rows_per_wg}")
+    seed = 12000 + d + Nq + 7 * Nk + B
+    qi = make_inputs(WORKLOADS[3], B=B, H=H, N=Nq, d=d, seed=seed, dtype=DTYPES[dt])
+    ki = qi if Nk == Nq else make_inputs(WORKLOADS[3], B=B, H=H, N=Nk, d=d, seed=seed + 1,
+                                         dtype=DTYPES[dt])
+    dev = torch.device("cuda:0")
+    o, lse = mi.attn_fwd_ex(qi["q"].to(dev), ki["k"].to(dev), ki["v"].to(dev),
+                            scale=qi["scale"], causal=causal)
+    torch.cuda.synchronize()
+    o, lse = o.float().cpu().numpy(), lse.cpu().numpy()
+    rng = np.random.default_rng(seed)
+    edges = [0, 31, 32, rows_per_wg - 1, rows_per_wg, Nq - 33, Nq - 1]
+    sample = np.unique(np.clip(np.concatenate([edges, rng.integers(0, Nq, 20)]), 0, Nq - 1))
+    pos = sample + (Nk - Nq)
+    for b, h in ((0, 0), (B - 1, H - 1)):
+        o_ref, lse_ref = attend_head(as64(qi["q"][b, h, sample]), as64(ki["k"][b, h]),
+                                     as64(ki["v"][b, h]), qi["scale"], causal, q_pos=pos)
+        check_with_empty_rows(o[b, h, sample], lse[b, h, sample], o_ref, lse_ref,
+                              f"head ({b},{h})")
