@@ -74,6 +74,17 @@ int pick_waves(int64_t BH, int Nq, int Nk, int d, bool causal) {
   return 8;
 }
 
+// The dQ kernel at d = 128 runs the ping-pong form (256 queries a
+// workgroup) with the eight-wave shape, and with the causal mask under the
+// same size conditions on the query side (the key-side kernel then keeps
+// four waves, which lost less there).
+bool pick_dq_pp(int64_t BH, int Nq, int Nk, int d, bool causal, int nw) {
+  if (d != 128) return false;
+  if (!causal) return nw == 8;
+  if (Nq < 2048 || Nk < 2048 || BH * (((int64_t)Nq + 255) / 256) < 2 * kCUs) return false;
+  return (int64_t)(Nq > Nk ? Nq : Nk) * d * 2 + (int64_t)256 * d * 2 <= INT32_MAX;
+}
+
 template <typename E>
 hipError_t launch_bwd_type(const BwdArgs& a, int d, bool causal) {
   switch (d) {
@@ -131,8 +142,9 @@ int bwd_run(const void* q, const void* k, const void* v, const void* o, const fl
   if ((int64_t)Nk * d * 2 + (int64_t)kBlockRows * d * 2 > INT32_MAX) return ATTN_ERR_SHAPE;
   const int64_t BH = (int64_t)B * H;
   const int nw = pick_waves(BH, Nq, Nk, d, causal != 0);
-  const int64_t rows = 32 * nw;
-  const int64_t nq = ((int64_t)Nq + rows - 1) / rows;
+  const bool dq_pp = pick_dq_pp(BH, Nq, Nk, d, causal != 0, nw);
+  const int64_t rows = 32 * nw, qrows = dq_pp ? 256 : rows;
+  const int64_t nq = ((int64_t)Nq + qrows - 1) / qrows;
   const int64_t nk = ((int64_t)Nk + rows - 1) / rows;
   if (BH * nq > INT32_MAX || BH * nk > INT32_MAX) return ATTN_ERR_SHAPE;
   if (use_scratch && BH * Nq > kScratchRows) return ATTN_ERR_SCRATCH;
@@ -166,7 +178,7 @@ int bwd_run(const void* q, const void* k, const void* v, const void* o, const fl
   }
 
   const BwdArgs a{q, k, v, o, d_o, lse, dq, dk, dv, delta, (int)BH, Nq, Nk, (int)nq, (int)nk,
-                  nw, scale * kLog2e, scale, static_cast<hipStream_t>(stream)};
+                  nw, dq_pp, scale * kLog2e, scale, static_cast<hipStream_t>(stream)};
   const hipError_t err = d == 256 ? launch_bwd_d256(a, causal != 0, dtype == ATTN_F16)
                          : dtype == ATTN_BF16 ? launch_bwd_type<__bf16>(a, d, causal != 0)
                                               : launch_bwd_type<_Float16>(a, d, causal != 0);

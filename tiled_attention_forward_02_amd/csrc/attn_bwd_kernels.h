@@ -25,6 +25,7 @@ struct BwdArgs {
   void *dq, *dk, *dv;
   float* delta;
   int BH, Nq, Nk, nq, nk, nw;
+  bool dq_pp;  // dQ by the ping-pong kernel (d = 128): nq counts its 256-row workgroups
   float c, scale;
   hipStream_t stream;
 };
@@ -316,8 +317,8 @@ __global__ __launch_bounds__(64 * NW, (kBwdMinBlocks<D, NW>)) void attn_bwd_dq_k
 }
 
 // --------------------------------------------- dQ ping-pong kernel (d = 128) --
-// The eight-wave shape at d = 128 without the causal mask: 256 queries a
-// workgroup, 32 a wave, one workgroup a CU; waves w and w + 4 share a SIMD.
+// The eight-wave dQ shape at d = 128: 256 queries a workgroup, 32 a wave, one
+// workgroup a CU; waves w and w + 4 share a SIMD.
 // Each wave alternates an MFMA phase M(t) (dQ^T += K^T dS^T of key tile
 // t-1, then S^T = K Q^T and dP^T = V dO^T of tile t) and a VALU phase X(t)
 // (P and dS of tile t), with a workgroup barrier after each; waves 4-7 run
@@ -330,14 +331,16 @@ __global__ __launch_bounds__(64 * NW, (kBwdMinBlocks<D, NW>)) void attn_bwd_dq_k
 // stages. Tile t + 2 is loaded during M(t): K by waves 0-3, V by waves 4-7,
 // three DMA instructions a wave (each part is padded from ten instructions
 // to twelve, the last two writing zeros past the rows, so no wave
-// branches). Operands are read three MFMAs ahead.
+// branches). Operands are read three MFMAs ahead. With the causal mask the
+// workgroup walks the key tiles up to its last row's; a wave whose rows see
+// none of a tile's keys (or only some) gets P = 0 for those keys, so its dQ
+// MFMAs add exact zeros and the MFMA sequence keeps no branch.
 template <typename E, bool CAUSAL>
 __global__ __launch_bounds__(512, 1) void attn_bwd_dq_pp_kernel(
     const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict__ V,
     const E* __restrict__ O, const float* __restrict__ LSE, const E* __restrict__ dO,
     E* __restrict__ dQ, float* __restrict__ Delta, int BH, int Nq, int Nk, int nq, float c,
     float dq_scale) {
-  static_assert(!CAUSAL, "the ping-pong dQ kernel runs without the causal mask");
   constexpr int D = 128, NW = 8, BN = 32, NST = 4, PD = 3;
   using G = SwzTile<D, BN, NW>;  // layout and reads of a tile part
   using GD = SwzTile<D, BN, 4>;  // its DMA, dealt to four waves
@@ -356,7 +359,9 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_pp_kernel(
   int bh, qt;
   map_block(blockIdx.x, BH, nq, CAUSAL, bh, qt);
   const int q0 = qt * 32 * NW;
-  const int qi = q0 + 32 * wave + col;
+  const int qw = q0 + 32 * wave;  // first query of this wave
+  const int qi = qw + col;
+  const int off = Nk - Nq;  // query i sees key j iff j <= i + off (causal)
 
   const size_t qhead = (size_t)bh * (size_t)Nq * D;
   const size_t khead = (size_t)bh * (size_t)Nk * D;
@@ -392,7 +397,8 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_pp_kernel(
     const rsrc_t rd = make_rsrc(Delta + (size_t)bh * Nq, (uint32_t)Nq * 4);
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(delta), rd, qi * 4, 0, 0);
   }
-  const int nt = Nk > 0 ? (Nk + BN - 1) / BN : 0;
+  const int kv_end = CAUSAL ? min(Nk, q0 + 32 * NW + off) : Nk;
+  const int nt = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
 
   const G tile(wave, lane);
   const GD dtile(dwave, lane);
@@ -463,16 +469,18 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_pp_kernel(
     }
     __builtin_amdgcn_s_setprio(0);
     barrier();
-    // P = 2^(s c - lse), 0 for keys past Nk, and dS^T = P^T (dP^T - D).
+    // P = 2^(s c - lse), 0 for keys past Nk (and, causal, past the row's
+    // last visible key), and dS^T = P^T (dP^T - D).
     const int k0 = t * BN;
     float p[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) p[i] = weight(sacc[i], c, l2);
-    if (k0 + BN > Nk) {
+    if ((k0 + BN > Nk) || (CAUSAL && k0 + BN - 1 > qw + off)) {
+      const int lim = CAUSAL ? min(Nk - 1, qi + off) : Nk - 1;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int key = k0 + 8 * (i >> 2) + 4 * half + (i & 3);
-        if (key >= Nk) p[i] = 0.f;
+        if (key > lim) p[i] = 0.f;
       }
     }
 #pragma unroll
@@ -764,11 +772,18 @@ hipError_t launch_bwd(const BwdArgs& a) {
   if (nq > 0) {
     void* args[] = {&q, &k, &v, &o, &lse, &d_o, &dq, &delta, &BH, &Nq, &Nk, &nq, &c, &scale};
     const void* fn;
-    if constexpr (D == 128 && NW == 8 && !CAUSAL)
+    int threads = 64 * NW;
+    if constexpr (D == 128 && NW == 8) {  // the eight-wave shape: always the ping-pong dQ
       fn = reinterpret_cast<const void*>(&attn_bwd_dq_pp_kernel<E, CAUSAL>);
-    else
+      threads = 512;
+    } else if constexpr (D == 128) {
+      fn = a.dq_pp ? reinterpret_cast<const void*>(&attn_bwd_dq_pp_kernel<E, CAUSAL>)
+                   : reinterpret_cast<const void*>(&attn_bwd_dq_kernel<E, D, CAUSAL, NW>);
+      threads = a.dq_pp ? 512 : 64 * NW;
+    } else {
       fn = reinterpret_cast<const void*>(&attn_bwd_dq_kernel<E, D, CAUSAL, NW>);
-    const hipError_t err = hipLaunchKernel(fn, dim3(BH * nq), dim3(64 * NW), args, 0, a.stream);
+    }
+    const hipError_t err = hipLaunchKernel(fn, dim3(BH * nq), dim3(threads), args, 0, a.stream);
     if (err != hipSuccess) return err;
   }
   if (nk > 0) {
