@@ -617,6 +617,11 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_pp_kernel(
   constexpr int QB = D == 256 ? 1 : 2, NW = 8, NST = 3;
   constexpr int BN = D == 64 ? 64 : 32;       // keys per tile: 8 KiB of K, 8 of V (16 at d = 256)
   constexpr int NKB = BN / 32;                // 32-key blocks per tile
+  // The MFMA phase runs at raised wave priority, so that its MFMAs go first
+  // when the softmax wave of the SIMD also has work; not at d = 64, whose
+  // softmax phase is the longer one (without it +0.7% to +1.6% on three
+  // d = 64 shapes, two boxes; with it at d = 128, 96 and 256 +0.6% to +3.8%).
+  constexpr bool kPhasePrio = D != 64;
   constexpr int NDB = D / 32;                 // 32-column blocks of O
   constexpr int DL = D == 96 ? 128 : D;       // row width in LDS (d = 96: chunks 12-15 zero)
   constexpr uint32_t ROWB = DL * 2;           // bytes per row in LDS
@@ -943,7 +948,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_pp_kernel(
     constexpr uint32_t bnext = ((st + 1) % NST) * SB;
     const bool do_s = t < wave_nt;
     refresh();
-    __builtin_amdgcn_s_setprio(1);
+    if constexpr (kPhasePrio) __builtin_amdgcn_s_setprio(1);
     // The first three K fragments of tile t are read while the last P*V
     // pairs run (always: the stage holds tile t either way).
     v8 g[4];
@@ -1009,7 +1014,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_pp_kernel(
         issue_dma();
       }
     }
-    __builtin_amdgcn_s_setprio(0);
+    if constexpr (kPhasePrio) __builtin_amdgcn_s_setprio(0);
     barrier();
     if constexpr (kPrepAhead) dma_prep((t + 1 + (late ? 2 : 1)) * BN);  // for M(t+1)
     if (do_s) {
