@@ -215,35 +215,43 @@ def test_bwd_one_side_empty():
     assert bool((dq == 0).all()) and dk.numel() == 0 and dv.numel() == 0
 
 
-@pytest.mark.parametrize("Nq,Nk", [(2100, 2100), (2100, 2200)])
-def test_bwd_eight_wave_workgroups(Nq, Nk):
-    """d = 128 without the mask, B*H = 64 heads of at least 2048 rows: both
-    kernels run eight-wave workgroups (256 rows or keys; B*H*ceil(N/256) >=
-    512), the last one ragged. Two heads
-    against the oracle, and four heads bit-identical to a call on just those
-    heads, whose small grid runs four-wave workgroups: each row's dq and each
-    key's dk, dv take the same tiles in the same order either way. The
-    two-head calls get the big call's o and lse."""
-    announce(f"bwd eight-wave workgroups Nq={Nq} Nk={Nk} d=128")
+EIGHT_WAVE = [(2100, 2100, False), (2100, 2200, False),
+              (2100, 2100, True), (2100, 2300, True), (2300, 2100, True)]
+
+
+@pytest.mark.parametrize("Nq,Nk,causal", EIGHT_WAVE)
+def test_bwd_eight_wave_workgroups(Nq, Nk, causal):
+    """d = 128, B*H = 64 heads of at least 2048 rows and keys
+    (B*H*ceil(Nq/256) >= 512): the dQ side runs eight-wave workgroups of 256
+    rows, the last one ragged, with or without the mask; without it the key
+    side does too. With the mask and Nk < Nq the first Nq - Nk rows see no key
+    (their dq is zero), and a workgroup's waves can stop at different keys.
+    Two heads against the oracle, and four heads bit-identical to a call on
+    just those heads, whose small grid runs four-wave workgroups: each row's
+    dq and each key's dk, dv take the same tiles in the same order either
+    way. The two-head calls get the big call's o and lse."""
+    announce(f"bwd eight-wave workgroups Nq={Nq} Nk={Nk} d=128 causal={causal}")
     dev = torch.device("cuda:0")
     qi = make_inputs(WORKLOADS[1], B=4, H=16, N=Nq, d=128, seed=23000 + Nq)
     ki = make_inputs(WORKLOADS[1], B=4, H=16, N=Nk, d=128, seed=24000 + Nk)
     do = upstream(qi["q"].shape, 25000 + Nk, torch.bfloat16)
     scale = qi["scale"]
     q, k, v, dog = qi["q"].to(dev), ki["k"].to(dev), ki["v"].to(dev), do.to(dev)
-    o, lse = mi.attn_fwd_ex(q, k, v, scale=scale)
-    big = mi.attn_bwd(q, k, v, o, lse, dog, scale=scale)
+    o, lse = mi.attn_fwd_ex(q, k, v, scale=scale, causal=causal)
+    big = mi.attn_bwd(q, k, v, o, lse, dog, scale=scale, causal=causal)
     torch.cuda.synchronize()
     for b, hs in ((0, slice(0, 2)), (3, slice(14, 16))):
         part = mi.attn_bwd(*(t[b:b + 1, hs].contiguous() for t in (q, k, v, o, lse, dog)),
-                           scale=scale)
+                           scale=scale, causal=causal)
         torch.cuda.synchronize()
         for name, x, y in zip(("dq", "dk", "dv"), big, part):
             assert torch.equal(x[b:b + 1, hs], y), f"batch {b} heads {hs}: {name} differs"
     q64, k64, v64, do64 = (as64(t) for t in (qi["q"], ki["k"], ki["v"], do))
     dq, dk, dv = (t.float().cpu().numpy() for t in big)
+    if causal and Nk < Nq:
+        assert not dq[:, :, :Nq - Nk].any(), "rows that see no key have a nonzero dq"
     for b, h in ((0, 0), (3, 15)):
-        rq, rk, rv = attend_head_grad(q64[b, h], k64[b, h], v64[b, h], do64[b, h], scale, False)
+        rq, rk, rv = attend_head_grad(q64[b, h], k64[b, h], v64[b, h], do64[b, h], scale, causal)
         check_grad(dq[b, h], rq, f"({b},{h}) dq")
         check_grad(dk[b, h], rk, f"({b},{h}) dk")
         check_grad(dv[b, h], rv, f"({b},{h}) dv")
