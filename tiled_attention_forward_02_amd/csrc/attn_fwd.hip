@@ -36,13 +36,14 @@
 // (ds_read_b64_tr_b16) hand each lane the V^T column it needs, 4 keys at a
 // time, in that permuted order.
 //
-// The running maximum is raised lazily. At d >= 64 the weights of a tile are
-// computed against the current reference maximum straight away, and the
-// reference moves (the tile's row maximum taken, O and the row sum rescaled,
-// the weights redone) only on the first tile or when a lane's share of the
-// tile's weights exceeds 2^12. At d = 32 the tile's row maximum comes first,
-// and the reference moves only when it exceeds the reference by more than
-// 2^8 (log2 units). Either way O / l and m + log2(l) stay exact in real
+// The running maximum is raised lazily. The first tile's row maximum is the
+// first reference (O and the row sum are still zero then). After that, at
+// d >= 64 the weights of a tile are computed against the current reference
+// maximum straight away, and the reference moves (the tile's row maximum
+// taken, O and the row sum rescaled, the weights redone) only when a lane's
+// share of the tile's weights exceeds 2^12. At d = 32 the tile's row maximum
+// comes first, and the reference moves only when it exceeds the reference by
+// more than 2^8 (log2 units). Either way O / l and m + log2(l) stay exact in real
 // arithmetic, because O and l always share one reference maximum. Masking
 // (causal diagonal tiles and the tile holding key N-1) is the only
 // per-element select, and only those tiles run it.
@@ -384,8 +385,11 @@ __global__ __launch_bounds__(64 * NW, (kMinBlocks<D, QB, NW>)) void attn_fwd_ker
   }
 
   // One tile: S^T, mask, running max, P, O^T += V^T P^T; then stage the next.
-  auto step = [&](int t, auto stage_c) {
+  // `first_c`: the first tile (t = 0), which every wave that sees a key
+  // computes.
+  auto step = [&](int t, auto stage_c, auto first_c) {
     constexpr int stage = decltype(stage_c)::value;
+    constexpr bool first = decltype(first_c)::value;
     constexpr uint32_t base = stage * T::STAGE * 2;
     const int k0 = t * BN;
     const bool has_next = t + 1 < nt;
@@ -489,20 +493,26 @@ __global__ __launch_bounds__(64 * NW, (kMinBlocks<D, QB, NW>)) void attn_fwd_ker
           for (int db = 0; db < D / 32; ++db) oacc[b][db] *= alpha;
           m_run[b] = m_new;
         };
-        if constexpr (kSpeculativeWeights<D>) {
+        if constexpr (first) {
+          // The tile's row maximum becomes the reference. O and l are still
+          // zero, so there is nothing to rescale (a rebase would multiply
+          // them by 0, or by 1 in a row that sees none of the tile's keys).
+          m_run[b] = fmaxf(m_run[b], tile_max());
+          weights();
+        } else if constexpr (kSpeculativeWeights<D>) {
           // Weights against the current reference, without the tile's own
           // maximum. The reference moves only when this lane's share of the
           // tile's weights exceeds kLazySum (every weight then stayed below
-          // it), and always on the first tile, where m_run = -inf: the tile's
-          // true row maximum becomes the reference and the weights are redone.
+          // it): the tile's true row maximum becomes the reference and the
+          // weights are redone.
           weights();
-          if (t == 0 || __any(tsum > kLazySum)) {
+          if (__any(tsum > kLazySum)) {
             rebase(fmaxf(m_run[b], tile_max()));
             weights();
           }
         } else {
           // Move the reference only when the tile's row maximum exceeds it by
-          // more than kLazyMax (always on the first tile).
+          // more than kLazyMax.
           const float m_tile = tile_max();
           if (__any(m_tile > m_run[b] + kLazyMax)) rebase(fmaxf(m_run[b], m_tile));
           weights();
@@ -546,9 +556,10 @@ __global__ __launch_bounds__(64 * NW, (kMinBlocks<D, QB, NW>)) void attn_fwd_ker
   lds_store(std::integral_constant<int, 0>{});
   if constexpr (kKDma<D> || kVDma<D>) __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  for (int t = 0; t < nt; t += 2) {
-    step(t, std::integral_constant<int, 0>{});
-    if (t + 1 < nt) step(t + 1, std::integral_constant<int, 1>{});
+  if (nt > 0) step(0, std::integral_constant<int, 0>{}, std::true_type{});
+  for (int t = 1; t < nt; t += 2) {
+    step(t, std::integral_constant<int, 1>{}, std::false_type{});
+    if (t + 1 < nt) step(t + 1, std::integral_constant<int, 0>{}, std::false_type{});
   }
 
   // Epilogue: O = acc / l (bf16), lse = (m + log2 l) * ln 2. Rows past N are
@@ -805,7 +816,9 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_pp_kernel(
   // two query blocks' weights are computed interleaved (the wave runs this
   // phase alone on its SIMD's VALU, so it needs the independent work); each
   // block's sum keeps its own order.
-  auto softmax = [&](f32x16 (&sacc)[QB][NKB], int t) __attribute__((always_inline)) {
+  auto softmax = [&](f32x16 (&sacc)[QB][NKB], int t, auto first_c)
+      __attribute__((always_inline)) {
+    constexpr bool first = decltype(first_c)::value;
     const int k0 = t * BN;
     if ((k0 + BN > Nk) || (CAUSAL && k0 + BN - 1 > qw + off)) {
 #pragma unroll
@@ -850,14 +863,18 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_pp_kernel(
         for (int i = 0; i < 16; ++i) weight(b, kb, i);
       tsum[b] = (part[b][0] + part[b][1]) + (part[b][2] + part[b][3]);
     };
-    auto rebase = [&](int b) __attribute__((always_inline)) {
+    // The reference raised to the tile's row maximum (log2 units).
+    auto raised = [&](int b) __attribute__((always_inline)) {
       float mx = fmaxf(sacc[b][0][0], sacc[b][0][1]);
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int i = kb ? 0 : 2; i < 16; i += 2)
           mx = fmaxf(mx, fmaxf(sacc[b][kb][i], sacc[b][kb][i + 1]));
-      const float m_new = fmaxf(m_run[b], swap_halves_max(mx) * c);
+      return fmaxf(m_run[b], swap_halves_max(mx) * c);
+    };
+    auto rebase = [&](int b) __attribute__((always_inline)) {
+      const float m_new = raised(b);
       const float alpha = __builtin_amdgcn_exp2f(m_run[b] - m_new);
       l_run[b] *= alpha;
 #pragma unroll
@@ -865,6 +882,12 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_pp_kernel(
       m_run[b] = m_new;
       weights(b);
     };
+    // The first tile's row maximum is the first reference; O and l are
+    // still zero, so nothing is rescaled.
+    if constexpr (first) {
+#pragma unroll
+      for (int b = 0; b < QB; ++b) m_run[b] = raised(b);
+    }
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -873,19 +896,19 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_pp_kernel(
         for (int b = 0; b < QB; ++b) weight(b, kb, i);
 #pragma unroll
     for (int b = 0; b < QB; ++b) tsum[b] = (part[b][0] + part[b][1]) + (part[b][2] + part[b][3]);
-    if constexpr (kJointRebase) {
+    if constexpr (!first && kJointRebase) {
       float worst = tsum[0];
 #pragma unroll
       for (int b = 1; b < QB; ++b) worst = fmaxf(worst, tsum[b]);
       // A block that did not need it is rebased too: exact, and rare.
-      if (t == 0 || __any(worst > kLazySum)) {
+      if (__any(worst > kLazySum)) {
 #pragma unroll
         for (int b = 0; b < QB; ++b) rebase(b);
       }
-    } else {
+    } else if constexpr (!first) {
 #pragma unroll
       for (int b = 0; b < QB; ++b)
-        if (t == 0 || __any(tsum[b] > kLazySum)) rebase(b);
+        if (__any(tsum[b] > kLazySum)) rebase(b);
     }
 #pragma unroll
     for (int b = 0; b < QB; ++b) l_run[b] += tsum[b];
@@ -1018,7 +1041,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_pp_kernel(
     barrier();
     if constexpr (kPrepAhead) dma_prep((t + 1 + (late ? 2 : 1)) * BN);  // for M(t+1)
     if (do_s) {
-      softmax(sacc, t);
+      softmax(sacc, t, first_c);
     } else {
 #pragma unroll
       for (int b = 0; b < QB; ++b)
