@@ -39,7 +39,10 @@ weights (masked entries 0):
   dV = P^T dO;  dP = dO V^T;  dS = P * (dP - rowsum(P * dP));
   dQ = scale * dS K;  dK = scale * dS^T Q.
 The last factor of dS is the Jacobian-vector product of a softmax row. A row
-that sees no key has P = 0 and contributes nothing.
+that sees no key has P = 0 and contributes nothing. Because O = P V, that row
+term also equals rowsum(dO * O): a backward handed the stored output O (as
+the FlashAttention backward is) may form it from O, and ``attend_head_grad``
+does so when given an ``o``.
 """
 
 from __future__ import annotations
@@ -123,13 +126,18 @@ def attention_ref(q, k, v, scale, causal):
     return o, lse
 
 
-def attend_head_grad(q, k, v, do, scale, causal, q_pos=None, chunk=1024):
+def attend_head_grad(q, k, v, do, scale, causal, q_pos=None, chunk=1024, o=None):
     """Gradients of one head: returns (dq [M,d], dk [N,d], dv [N,d]) in float64,
     of L = sum(do * o) with o the output of attend_head(q, k, v, scale, causal).
 
     The weights are recomputed from the definition exactly as attend_head
     forms them (full score rows, masked entries -inf, max subtracted); then
     the chain rule of the module docstring. q_pos as for attend_head.
+
+    o: optional [M, d] stored forward output. When given, each row's softmax
+    term is rowsum(do * o) instead of rowsum(P * dP): the same value for the
+    exact output, and for a rounded one the result of the backward formula
+    applied to the output it is handed.
 
     L is a sum over query rows, and a row's weights depend on that row alone,
     so the rows are taken ``chunk`` at a time only to bound memory: each chunk
@@ -148,6 +156,10 @@ def attend_head_grad(q, k, v, do, scale, causal, q_pos=None, chunk=1024):
     if q_pos is None:
         q_pos = np.arange(m_rows) + (n_keys - m_rows)
     q_pos = np.asarray(q_pos, dtype=np.int64)
+    if o is not None:
+        o = np.asarray(o, dtype=np.float64)
+        if o.shape != do.shape:
+            raise ValueError("o must be shaped like do")
 
     dq = np.empty((m_rows, d), dtype=np.float64)
     dk = np.zeros((n_keys, d), dtype=np.float64)
@@ -172,7 +184,11 @@ def attend_head_grad(q, k, v, do, scale, causal, q_pos=None, chunk=1024):
 
         dv += p.T @ do[r0:r1]
         dp = do[r0:r1] @ v.T
-        ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+        if o is None:
+            row = (p * dp).sum(axis=1, keepdims=True)
+        else:
+            row = (do[r0:r1] * o[r0:r1]).sum(axis=1, keepdims=True)
+        ds = p * (dp - row)
         dq[r0:r1] = scale * (ds @ k)
         dk += scale * (ds.T @ q[r0:r1])
     return dq, dk, dv

@@ -381,6 +381,40 @@ def test_mutant_harness_reproduces_the_oracle():
     assert all(p(clean) for p in PINS)
 
 
+# ------------------------------------------------- the stored-output form --
+
+@pytest.mark.parametrize("m,n", [(25, 25), (25, 40), (40, 25), (1, 2), (9, 1)])
+def test_stored_output_form_equals_the_definition(m, n):
+    """Given the exact output o (from attend_head), the row term rowsum(do * o)
+    equals rowsum(P * dP) because o = P v, so the gradients agree with the
+    plain form; small chunks check that o is sliced with its rows, and causal
+    Nq > Nk includes rows that see no key (o = 0, no contribution)."""
+    q, k, v, do = _rand((m, 6), 120), _rand((n, 6), 121), _rand((n, 6), 122), _rand((m, 6), 123)
+    for causal in (False, True):
+        o, _ = attend_head(q, k, v, 0.7, causal)
+        ref = attend_head_grad(q, k, v, do, 0.7, causal)
+        for chunk in (1, 4, 1024):
+            got = attend_head_grad(q, k, v, do, 0.7, causal, chunk=chunk, o=o)
+            for g, r in zip(got, ref):
+                assert np.allclose(g, r, rtol=0, atol=1e-12)
+
+
+def test_stored_output_moves_only_the_softmax_term():
+    """dv = P^T do does not involve the output at all, and a rounded output
+    moves dq and dk by an amount that vanishes with the rounding."""
+    q, k, v, do = _rand((12, 5), 130), _rand((9, 5), 131), _rand((9, 5), 132), _rand((12, 5), 133)
+    o, _ = attend_head(q, k, v, 0.5, True)
+    ref = attend_head_grad(q, k, v, do, 0.5, True)
+    rounded = np.round(o * 256) / 256
+    got = attend_head_grad(q, k, v, do, 0.5, True, o=rounded)
+    assert np.array_equal(got[2], ref[2])
+    assert not np.allclose(got[0], ref[0], rtol=0, atol=1e-12)
+    for g, r in zip(got[:2], ref[:2]):
+        assert np.abs(g - r).max() <= 1e-2 * np.abs(r).max()
+    with pytest.raises(ValueError):
+        attend_head_grad(q, k, v, do, 0.5, True, o=o[:, :4])
+
+
 # ------------------------------------------------------------------ plumbing --
 
 def test_batched_equals_per_head():
