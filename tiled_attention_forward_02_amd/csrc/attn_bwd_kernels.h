@@ -544,8 +544,8 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_pp_kernel(
 // ---------------------------------------------------------- dK/dV kernel --
 
 // One pass accumulates both dK and dV: the K and V fragments and the two
-// accumulators fit two waves per SIMD at every head dimension (256 VGPRs at
-// d = 128, with two values spilled outside the loop).
+// accumulators fit two waves per SIMD at every head dimension (248 VGPRs at
+// d = 128, 254 with the causal mask, no spills).
 
 // LDS stage of the key-side kernel:
 //   Q (rows: S = Q K^T; columns: dK) | dO (rows: dP; columns: dV) | lse | D
@@ -637,12 +637,14 @@ __global__ __launch_bounds__(64 * NW, (kBwdMinBlocks<D, NW>)) void attn_bwd_kv_k
       draw = __builtin_amdgcn_raw_buffer_load_b32(rd, qrow * 4, 0, 0);
     }
   };
+  // D goes in negated: it starts the dP accumulator, so dP - D comes out of
+  // the MFMA chain with no subtraction per element.
   auto lds_store = [&](auto stage_c) __attribute__((always_inline)) {
     constexpr uint32_t base = decltype(stage_c)::value * STAGE;
     if (tid < BQ) {
       *reinterpret_cast<float*>(lds + base + S_::L_OFF + tid * 4) =
           lse_log2(__uint_as_float(lraw), lvalid);
-      *reinterpret_cast<uint32_t*>(lds + base + S_::D_OFF + tid * 4) = draw;
+      *reinterpret_cast<uint32_t*>(lds + base + S_::D_OFF + tid * 4) = draw ^ 0x80000000u;
     }
   };
   f32x16 dkacc[D / 32], dvacc[D / 32];
@@ -660,12 +662,23 @@ __global__ __launch_bounds__(64 * NW, (kBwdMinBlocks<D, NW>)) void attn_bwd_kv_k
 
     // Some query of the tile sees a key of this wave.
     if (!CAUSAL || q0 + BQ - 1 + off >= kw) {
-      // S = Q K^T (and dP = dO V^T for dK), 32 queries per accumulator.
+      // S = Q K^T (and dP - D = dO V^T - D for dK, the chain started at -D),
+      // 32 queries per accumulator. Register i of block qb holds query
+      // q0 + 32qb + 8(i/4) + 4h + i%4: its lse and -D come four at a time
+      // from LDS.
       f32x16 sacc[NQB], pacc[NQB];
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb) {
         sacc[qb] = f32x16{};
-        pacc[qb] = f32x16{};
+        if constexpr (PART != 1) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int row = 32 * qb + 8 * r + 4 * half;
+            const f32x4 nd4 = *reinterpret_cast<const f32x4*>(lds + base + S_::D_OFF + row * 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) pacc[qb][4 * r + e] = nd4[e];
+          }
+        }
 #pragma unroll
         for (int j = 0; j < D / 16; ++j) {
           sacc[qb] = Elem<E>::mfma(tile.template rows<v8>(lds + base, qb, j), kf[j], sacc[qb]);
@@ -674,8 +687,6 @@ __global__ __launch_bounds__(64 * NW, (kBwdMinBlocks<D, NW>)) void attn_bwd_kv_k
                                      vf[j], pacc[qb]);
         }
       }
-      // Register i of block qb holds query q0 + 32qb + 8(i/4) + 4h + i%4: its
-      // lse and D come four at a time from LDS.
       const bool masked = CAUSAL && q0 + off < kw + 31;
       v8 pb[NQB][2], dsb[NQB][2];
 #pragma unroll
@@ -684,14 +695,13 @@ __global__ __launch_bounds__(64 * NW, (kBwdMinBlocks<D, NW>)) void attn_bwd_kv_k
         for (int r = 0; r < 4; ++r) {
           const int row = 32 * qb + 8 * r + 4 * half;
           const f32x4 l4 = *reinterpret_cast<const f32x4*>(lds + base + S_::L_OFF + row * 4);
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(lds + base + S_::D_OFF + row * 4);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int i = 4 * r + e;
             float p = weight(sacc[qb][i], c, l4[e]);
             if (masked && kj > q0 + row + e + off) p = 0.f;
             if constexpr (PART != 2) pb[qb][i >> 3][i & 7] = (E)p;
-            if constexpr (PART != 1) dsb[qb][i >> 3][i & 7] = (E)(p * (pacc[qb][i] - d4[e]));
+            if constexpr (PART != 1) dsb[qb][i >> 3][i & 7] = (E)(p * pacc[qb][i]);
           }
         }
       // dV^T += dO^T P and dK^T += Q^T dS, 16 queries per MFMA.
