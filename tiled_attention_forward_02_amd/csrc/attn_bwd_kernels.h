@@ -232,6 +232,14 @@ __global__ __launch_bounds__(64 * NW, (kBwdMinBlocks<D, NW>)) void attn_bwd_dq_k
   f32x16 acc[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
+  // -D in every register of a block: the first dP^T MFMA of each tile reads
+  // it as its accumulator input, so dP^T - D comes out of the chain with no
+  // subtraction per element. Its 16 registers stay live throughout; at
+  // d = 32 they would cost the fourth wave per SIMD, so d = 32 subtracts.
+  constexpr bool kNegD = D >= 64;
+  f32x16 negd;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) negd[i] = kNegD ? -delta : 0.f;
 
   auto step = [&](int t, auto stage_c) __attribute__((always_inline)) {
     constexpr uint32_t base = decltype(stage_c)::value * STAGE;
@@ -240,17 +248,16 @@ __global__ __launch_bounds__(64 * NW, (kBwdMinBlocks<D, NW>)) void attn_bwd_dq_k
     if (has_next) stage_tile(std::integral_constant<int, decltype(stage_c)::value ^ 1>{}, k0 + BN);
 
     if (k0 < wave_kv_end) {
-      // S^T = K Q^T and dP^T = V dO^T, 32 keys per accumulator.
+      // S^T = K Q^T and dP^T = V dO^T (less D), 32 keys per accumulator.
       f32x16 sacc[NKB], pacc[NKB];
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
-        sacc[kb] = f32x16{};
-        pacc[kb] = f32x16{};
 #pragma unroll
         for (int j = 0; j < D / 16; ++j) {
-          sacc[kb] = Elem<E>::mfma(tile.template rows<v8>(lds + base, kb, j), qf[j], sacc[kb]);
-          pacc[kb] = Elem<E>::mfma(tile.template rows<v8>(lds + base + V_OFF, kb, j), df[j],
-                                   pacc[kb]);
+          const v8 ka = tile.template rows<v8>(lds + base, kb, j);
+          const v8 va = tile.template rows<v8>(lds + base + V_OFF, kb, j);
+          sacc[kb] = Elem<E>::mfma(ka, qf[j], j == 0 ? f32x16{} : sacc[kb]);
+          pacc[kb] = Elem<E>::mfma(va, df[j], j == 0 ? (kNegD ? negd : f32x16{}) : pacc[kb]);
         }
       }
       // P, with 0 for keys past Nk and (causal) keys after the query.
@@ -273,7 +280,8 @@ __global__ __launch_bounds__(64 * NW, (kBwdMinBlocks<D, NW>)) void attn_bwd_dq_k
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) dsb[kb][i >> 3][i & 7] = (E)(p[kb][i] * (pacc[kb][i] - delta));
+        for (int i = 0; i < 16; ++i)
+          dsb[kb][i >> 3][i & 7] = (E)(p[kb][i] * (kNegD ? pacc[kb][i] : pacc[kb][i] - delta));
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -414,6 +422,11 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_pp_kernel(
   f32x16 acc[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
+  // -D in every register of a block: the accumulator input of each tile's
+  // first dP^T MFMA, so dP^T - D needs no subtraction per element.
+  f32x16 negd;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) negd[i] = -delta;
   // dS of the last tile (the B operand of dQ), and the first operands of the
   // next MFMA phase, read at the end of the VALU phase.
   v8 dsb[2];
@@ -441,7 +454,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_pp_kernel(
     constexpr uint32_t bcur = st * STAGE, bprev = ((st + 3) % NST) * STAGE;
     constexpr uint32_t bload = ((st + 2) % NST) * STAGE;
     constexpr int k_begin = first ? 8 : 0;
-    f32x16 sacc = f32x16{}, pacc = f32x16{};
+    f32x16 sacc, pacc;  // S^T and dP^T - D of tile t
     v8 f[PD + 1];
 #pragma unroll
     for (int i = 0; i < PD; ++i) f[i] = first ? operand(bprev, bcur, k_begin + i) : pre[i];
@@ -455,9 +468,9 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_pp_kernel(
       } else {
         const int j = (k - 8) / 2;
         if (k & 1)
-          pacc = Elem<E>::mfma(a, df[j], pacc);
+          pacc = Elem<E>::mfma(a, df[j], j == 0 ? negd : pacc);
         else
-          sacc = Elem<E>::mfma(a, qf[j], sacc);
+          sacc = Elem<E>::mfma(a, qf[j], j == 0 ? f32x16{} : sacc);
       }
       // Tile t + 2 (zeros past Nk) into the stage tile t - 2 left, after the
       // first S step.
@@ -484,7 +497,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_pp_kernel(
       }
     }
 #pragma unroll
-    for (int i = 0; i < 16; ++i) dsb[i >> 3][i & 7] = (E)(p[i] * (pacc[i] - delta));
+    for (int i = 0; i < 16; ++i) dsb[i >> 3][i & 7] = (E)(p[i] * pacc[i]);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < PD; ++i) pre[i] = operand(bcur, 0, i);
